@@ -1,0 +1,112 @@
+"""Seeded synthetic inputs shared by the GPU path's tests, the oracle's tests
+and the benchmark.
+
+This module draws random numbers and casts them to the storage dtype; it holds
+none of the attention arithmetic. Recipe (the pages fix no seeds or
+distributions beyond the shapes):
+
+* ``numpy.random.default_rng(seed)`` (PCG64, stable across numpy versions);
+* ``standard_normal(shape, dtype=float32)`` in the storage order of the
+  layout, drawn in the order q, k, v, then the per-sequence key lengths;
+* an optional float32 multiplier on q and k (the long causal workload uses
+  2.0 to widen the score spread);
+* per-sequence key lengths ``rng.integers(lo, hi + 1, size=B)`` when the
+  workload pads keys;
+* a round-to-nearest-even cast to the storage dtype with torch ``.to``.
+
+The oracle and the GPU path read exactly these quantised tensors.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    Sq: int
+    Sk: int
+    d: int
+    dtype: str            # "f32" | "f16" | "bf16"
+    layout: str           # "bhsd" | "bshd"
+    causal: bool = False
+    qk_mult: float = 1.0  # multiplier applied to q and k before the cast
+    kv_len_range: tuple[int, int] | None = None  # inclusive range of valid key counts
+    seed: int = 0
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def shape(self, S: int) -> tuple[int, int, int, int]:
+        if self.layout == "bhsd":
+            return (self.B, self.H, S, self.d)
+        return (self.B, S, self.H, self.d)
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads of the fused-forward study. The medium prefill shape is
+# the B=1, h=16, S=4096, D=1024 example of the memory table in §2.5 of the
+# self-attention chapter (d = 1024 / 16 = 64).
+WORKLOADS: dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("tiny_fp32", B=1, H=2, Sq=256, Sk=256, d=64, dtype="f32", layout="bhsd", seed=0,
+                 description="tiny non-causal fp32, B1 H2 S256 d64, [B,H,S,d]"),
+        Workload("medium_bf16", B=1, H=16, Sq=4096, Sk=4096, d=64, dtype="bf16", layout="bhsd",
+                 seed=1, description="medium prefill bf16, B1 H16 S4096 d64, [B,H,S,d], LSE out"),
+        Workload("long_causal_bf16", B=2, H=16, Sq=8192, Sk=8192, d=128, dtype="bf16",
+                 layout="bshd", causal=True, qk_mult=2.0, seed=2,
+                 description="long causal prefill bf16, B2 H16 S8192 d128, [B,S,H,d], q,k x2.0"),
+        Workload("bert_pad_fp16", B=32, H=12, Sq=512, Sk=512, d=64, dtype="f16", layout="bhsd",
+                 kv_len_range=(256, 512), seed=3,
+                 description="batched short fp16, B32 H12 S512 d64, key padding 256..512"),
+        Workload("decode_bf16", B=8, H=32, Sq=1, Sk=32768, d=128, dtype="bf16", layout="bhsd",
+                 seed=4, description="single-query decode bf16, B8 H32 Sq1 Sk32768 d128, split-K"),
+    ]
+}
+
+
+def generate(w: Workload, seed: int | None = None) -> dict:
+    """Draw q, k, v (torch CPU tensors in w.dtype and w.layout) and kv_len
+    (torch int32 [B] or None) for workload ``w``."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    tdt = DTYPES[w.dtype]
+    out = {}
+    for name, S in (("q", w.Sq), ("k", w.Sk), ("v", w.Sk)):
+        a = rng.standard_normal(w.shape(S), dtype=np.float32)
+        if name in ("q", "k") and w.qk_mult != 1.0:
+            a *= np.float32(w.qk_mult)
+        out[name] = torch.from_numpy(a).to(tdt)
+        del a
+    if w.kv_len_range is not None:
+        lo, hi = w.kv_len_range
+        out["kv_len"] = torch.from_numpy(rng.integers(lo, hi + 1, size=w.B).astype(np.int32))
+    else:
+        out["kv_len"] = None
+    return out
+
+
+def poison_padding(k: torch.Tensor, v: torch.Tensor, kv_len, layout: str) -> None:
+    """Fill the key/value rows at or beyond each sequence's valid length with
+    NaN, in place, so that any read of them shows up in the output."""
+    if kv_len is None:
+        return
+    for b, n in enumerate(torch.as_tensor(kv_len).tolist()):
+        if layout == "bhsd":
+            k[b, :, n:, :] = float("nan")
+            v[b, :, n:, :] = float("nan")
+        else:
+            k[b, n:, :, :] = float("nan")
+            v[b, n:, :, :] = float("nan")
