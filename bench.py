@@ -1,0 +1,221 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+Default (no flags): the medium prefill workload, B=1 H=16 Sq=Sk=4096 d=64,
+bf16, [B,H,S,d], non-causal, LSE out. One step = one attn_fwd call (the fused
+kernel: Q tile load, K/V streaming, QK^T, mask, online softmax, PV, epilogue).
+Prints one JSON line with the throughput in TFLOP/s, the roofline of the
+fused kernel and the fp64 oracle timed on the host cores.
+
+FLOPs per step: 4*B*H*Sq*Sk*d (two products of 2*d FLOPs per score), halved
+for causal masks. Inputs are resident in HBM before the timed region.
+
+Other workloads (--config) and the unfused baseline (--path naive) are for
+the design notes; only the default line is the headline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS_16 = 2516.6   # MI355X dense bf16/fp16 matrix peak: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_TFLOPS_F32 = 157.3   # MI355X fp32 peak
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def flops(w) -> float:
+    f = 4.0 * w.B * w.H * w.Sq * w.Sk * w.d
+    return f / 2 if w.causal else f
+
+
+def kv_bytes(w) -> float:
+    es = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+    return 2.0 * w.B * w.H * w.Sk * w.d * es
+
+
+def kernel_source_digest(path: str) -> str:
+    """Hash of the sources that define the timed kernels (for matching a
+    stored counter profile to the code it was taken on)."""
+    csrc = os.path.join(ROOT, "scaled_dot_product_flashattention_amd", "csrc")
+    files = {"fused": ["fwd_prefill.hip", "device_common.h"],
+             "splitk": ["fwd_splitk.hip", "device_common.h"],
+             "naive": ["naive.hip", "device_common.h"]}[path]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str, path: str):
+    """HBM bytes per launch from the committed counter profile of this
+    workload, or None when there is none or the kernel source changed since."""
+    fn = os.path.join(PROFILES, f"{workload}_{path}_traffic.json")
+    if not os.path.exists(fn):
+        return None
+    with open(fn) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_digest(path):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_share() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(w, t, target_s: float = 12.0):
+    """The fp64 oracle on a bounded sample of rows of the same workload,
+    timed on the host cores, scaled to the metric's unit."""
+    import numpy as np
+
+    import oracle
+
+    cores = cpu_share()
+    R = w.B * w.H * w.Sq
+    rng = np.random.default_rng(5)
+    n = min(R, 4 * cores)
+    while True:
+        rows = np.sort(rng.choice(R, size=n, replace=False))
+        t0 = time.perf_counter()
+        oracle.attention_rows(t["q"], t["k"], t["v"], rows, scale=w.scale, causal=w.causal,
+                              layout=w.layout, kv_len=t["kv_len"], nthreads=cores)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 4 or n >= R:
+            break
+        n = min(R, max(n * 2, int(n * target_s / max(dt, 1e-3))))
+    if w.causal:
+        i = rows % w.Sq
+        f = float(np.sum(4.0 * w.d * np.minimum(i + 1, w.Sk)))
+    else:
+        f = 4.0 * w.d * w.Sk * len(rows)
+    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(rows)} of {R} query rows of the same workload, full key range each, "
+                      f"{dt:.1f} s wall on {cores} threads (fp64, three-step softmax)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="medium_bf16")
+    ap.add_argument("--path", default="fused", choices=["fused", "naive", "splitk"])
+    ap.add_argument("--n-split", type=int, default=None)
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the fused kernel "
+              "is a single-GPU operation and multi-GPU runs are not part of this build.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import scaled_dot_product_flashattention_amd as sdpa
+    from scaled_dot_product_flashattention_amd.inputs import WORKLOADS, generate
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    w = WORKLOADS[args.config]
+    t = generate(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (t[n].to(dev) for n in ("q", "k", "v"))
+    kv_len = None if t["kv_len"] is None else t["kv_len"].to(dev)
+    B, H, Sq, Sk, d = w.B, w.H, w.Sq, w.Sk, w.d
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    kw = dict(scale=w.scale, causal=w.causal, layout=w.layout, kv_len=kv_len, out=o, lse=lse)
+    if args.path == "fused":
+        nbytes = sdpa.attn_fwd_workspace_size(B, H, Sq, Sk, d, q.dtype)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        step = lambda: sdpa.attn_fwd(q, k, v, workspace=ws, **kw)  # noqa: E731
+        n_split = sdpa.attn_fwd_plan(B, H, Sq, Sk, d, q.dtype)
+    elif args.path == "splitk":
+        n_split = args.n_split or sdpa.attn_fwd_plan(B, H, Sq, Sk, d, q.dtype)
+        ws = torch.empty(sdpa.attn_splitk_workspace_size(B, H, Sq, d, n_split), dtype=torch.uint8,
+                         device=dev)
+        step = lambda: sdpa.attn_fwd_splitk(q, k, v, n_split=n_split, workspace=ws, **kw)  # noqa: E731
+    else:
+        n_split = 1
+        sc = torch.empty(sdpa.attn_naive_scratch_size(B, H, Sq, Sk, q.dtype), dtype=torch.uint8,
+                         device=dev)
+        step = lambda: sdpa.attn_fwd_naive(q, k, v, scratch=sc, **kw)  # noqa: E731
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3
+    ms = e0.elapsed_time(e1) / args.steps
+
+    fl = flops(w)
+    decode = args.path == "splitk" or n_split > 1
+    tflops = fl / (ms * 1e-3) / 1e12
+    if decode:
+        achieved = kv_bytes(w) / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+        metric, value, unit = f"attention decode HBM GB/s, {w.description}", achieved, "GB/s"
+    else:
+        peak = PEAK_TFLOPS_F32 if w.dtype == "f32" else PEAK_TFLOPS_16
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tflops / peak, 4)}
+        if args.config == "medium_bf16" and args.path == "fused":
+            metric = "fused attention fwd TFLOP/s and % bf16 MFMA peak, B1 H16 S4096 d64"
+        else:
+            metric = f"attention fwd TFLOP/s ({args.path}), {w.description}"
+        value, unit = tflops, "TFLOP/s"
+    roof["traffic"] = stored_traffic(args.config, args.path)
+    roof["kernel_ms"] = round(ms, 5)
+    roof["algorithmic_units"] = ("bytes of K and V per launch" if decode else "FLOPs per launch")
+    roof["algorithmic_per_launch"] = kv_bytes(w) if decode else fl
+
+    line = {
+        "metric": metric,
+        "value": round(value, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "f16": "fp16", "bf16": "bf16"}[w.dtype],
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "B": B, "H": H, "Sq": Sq,
+                   "Sk": Sk, "d": d, "layout": w.layout, "causal": w.causal, "path": args.path,
+                   "n_split": n_split, "flops_per_step": fl, "wall_ms_timed_region": round(wall_ms, 2)},
+        "roofline": roof,
+    }
+    if not args.skip_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, t)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

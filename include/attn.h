@@ -1,0 +1,137 @@
+/*
+ * libattn: fused scaled-dot-product attention forward for MI355X (gfx950).
+ *
+ * Computes, for every batch b, head h and query row i,
+ *     S_ij = scale * q_i . k_j                 (scores)
+ *     P_ij = exp(S_ij - m_i) / l_i             (softmax along the keys)
+ *     O_i  = sum_j P_ij v_j                    (weighted sum)
+ *     LSE_i = m_i + ln l_i
+ * over the valid keys j of row i, where m_i is the row maximum and l_i the
+ * sum of the shifted exponentials. The definition is §2.2-§2.4 of the chapter
+ * "2. 自注意力机制算子：QKV投影、注意力分数计算、Softmax、加权求和，以及FlashAttention
+ * 优化"; the fused evaluation (tiles, running max and sum, rescale of the
+ * partial output by exp(m_old - m_new)) is its §2.6 and the section
+ * "FlashAttention 分块计算原理与浏览器适配" of "WebGPU 算子优化：QKV 内存合并与
+ * FlashAttention 分块计算". The score and probability matrices never reach
+ * device memory in attn_fwd / attn_fwd_splitk.
+ *
+ * Valid keys. Key j is valid for query i of sequence b iff j < n_b and, when
+ * `causal` is nonzero, j <= i (key j > query i is masked, counted from the
+ * first query and the first key, also when Sq != Sk). n_b = kv_len[b] clamped
+ * to [0, Sk], or Sk when kv_len is NULL. Rows with no valid key give O = 0
+ * and LSE = -inf. Key/value rows at or beyond n_b are never read.
+ *
+ * Tensors (all device memory, owned by the caller, never retained):
+ *   q, o   [B, H, Sq, d] (ATTN_LAYOUT_BHSD) or [B, Sq, H, d] (ATTN_LAYOUT_BSHD),
+ *          dense, element type `dtype`; o has the layout and type of q.
+ *   k, v   the same layout with Sk rows.
+ *   lse    float32 [B, H, Sq] whatever the layout, or NULL to skip it.
+ *   kv_len int32 [B] or NULL.
+ * The two layouts are the "Contiguous" and head-"Interleaved" QKV layouts of
+ * the section "QKV 矩阵的内存合并模式选择" of the WebGPU page, read as
+ * separate q, k, v tensors with heads outermost or interleaved per token.
+ * q, k, v, o and workspaces must be 16-byte aligned; lse and kv_len 4-byte.
+ *
+ * Arithmetic: bf16/fp16 inputs use bf16/fp16 matrix-core products with fp32
+ * accumulation; the softmax state is fp32; probabilities are rounded to the
+ * input type (nearest-even) before the second product; the output is rounded
+ * once to the input type. fp32 inputs keep every step in fp32.
+ *
+ * Execution: every call validates all arguments on the host first and
+ * returns an error status without touching the GPU when one is bad. On
+ * success it enqueues its kernels on `stream` (a hipStream_t; NULL is the
+ * null stream) and returns without synchronising; outputs are valid once the
+ * stream has reached that point. Launch failures return ATTN_E_HIP. The
+ * library holds no state and is safe to call from several threads; calls
+ * that share a workspace must be ordered by the caller.
+ */
+#ifndef LIBATTN_ATTN_H
+#define LIBATTN_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_E_NULLPTR = 1,     /* a required pointer is NULL                        */
+    ATTN_E_SHAPE = 2,       /* B, H, Sq or Sk < 1, n_split < 1, or sizes overflow */
+    ATTN_E_UNSUPPORTED = 3, /* d not 64 or 128, or an enum value out of range    */
+    ATTN_E_ALIGN = 4,       /* a pointer is not aligned as stated above          */
+    ATTN_E_WORKSPACE = 5,   /* workspace / scratch NULL or smaller than required */
+    ATTN_E_HIP = 6,         /* the HIP runtime reported an error at launch       */
+    ATTN_E_ARG = 7          /* scale is negative, NaN or infinite                */
+};
+
+enum attn_layout { ATTN_LAYOUT_BHSD = 0, ATTN_LAYOUT_BSHD = 1 };
+
+enum attn_dtype { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 };
+
+/*
+ * Fused forward. Chooses between one fused kernel (prefill shapes) and the
+ * split-over-keys pair of kernels (few query rows over many keys) as
+ * attn_fwd_plan reports; the split path needs `workspace` of at least
+ * attn_fwd_workspace_size bytes (NULL / 0 is fine when that size is 0).
+ * scale must be finite and >= 0 (0 gives uniform weights over the valid keys).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
+             int dtype, const int32_t* kv_len, void* workspace, size_t workspace_bytes,
+             void* stream);
+
+/* Bytes of workspace attn_fwd needs for this shape (0 when it plans no split).
+ * Returns 0 for arguments attn_fwd would reject. Host only. */
+size_t attn_fwd_workspace_size(int B, int H, int Sq, int Sk, int d, int dtype);
+
+/* The number of key splits attn_fwd will use (1 = single fused kernel).
+ * Host only; returns a status and writes *n_split on success. */
+int attn_fwd_plan(int B, int H, int Sq, int Sk, int d, int dtype, int* n_split);
+
+/*
+ * Split-over-keys forward with an explicit split count (the single-query
+ * decode path). The keys [0, Sk) are cut into n_split equal ranges; each
+ * (b, h, i, split) writes its unnormalised partial (running max, running
+ * sum, weighted sum of V) to the workspace, and a second kernel merges the
+ * partials of each row with weights exp(m_s - max_s m_s) — the block merge of
+ * the WebGPU page's FlashAttention section and §2.6 of the chapter. Splits
+ * with no valid key contribute nothing. Any n_split >= 1 is accepted.
+ */
+int attn_fwd_splitk(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
+                    int dtype, const int32_t* kv_len, int n_split, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for attn_fwd_splitk (0 for rejected arguments). Host only. */
+size_t attn_splitk_workspace_size(int B, int H, int Sq, int d, int n_split);
+
+/*
+ * Unfused baseline with the materialised intermediates of the chapter's §2.5:
+ * kernel 1 writes S = scale * Q K^T to scratch ([B, H, Sq, Sk], input type),
+ * kernel 2 runs the three-step softmax on each row (max, then sum, then
+ * normalise, each a pass over the stored row) and writes P (same shape and
+ * type) plus LSE, kernel 3 computes O = P V. Same arguments and results as
+ * attn_fwd; `scratch` must hold attn_naive_scratch_size bytes.
+ */
+int attn_fwd_naive(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
+                   int dtype, const int32_t* kv_len, void* scratch, size_t scratch_bytes,
+                   void* stream);
+
+/* Scratch bytes for attn_fwd_naive: S and P, 2 * B*H*Sq*Sk elements of dtype,
+ * plus alignment padding (0 for rejected arguments). Host only. */
+size_t attn_naive_scratch_size(int B, int H, int Sq, int Sk, int dtype);
+
+/* Static text for a status code. */
+const char* attn_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBATTN_ATTN_H */

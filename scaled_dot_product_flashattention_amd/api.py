@@ -1,0 +1,209 @@
+"""Python binding of libattn: the C-ABI entry points under the same names.
+
+Argument marshalling only. torch supplies device memory (outputs, workspaces)
+and the current stream; every step of the computation runs in libattn's HIP
+kernels. There is no fallback: a missing library raises ImportError and any
+nonzero status from the library raises AttnError.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+from .build import library_path
+
+_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+_LAYOUT = {"bhsd": 0, "bshd": 1}
+
+
+class AttnError(RuntimeError):
+    """A libattn call returned a nonzero status."""
+
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {attn_status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libattn.so from the package directory (built in-tree)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"libattn.so is not built at {path}; build it with "
+                          "`python -m scaled_dot_product_flashattention_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    tensors = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+    L.attn_fwd.argtypes = tensors + [vp, sz, vp]
+    L.attn_fwd.restype = i
+    L.attn_fwd_splitk.argtypes = tensors + [i, vp, sz, vp]
+    L.attn_fwd_splitk.restype = i
+    L.attn_fwd_naive.argtypes = tensors + [vp, sz, vp]
+    L.attn_fwd_naive.restype = i
+    L.attn_fwd_workspace_size.argtypes = [i, i, i, i, i, i]
+    L.attn_fwd_workspace_size.restype = sz
+    L.attn_fwd_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i)]
+    L.attn_fwd_plan.restype = i
+    L.attn_splitk_workspace_size.argtypes = [i, i, i, i, i]
+    L.attn_splitk_workspace_size.restype = sz
+    L.attn_naive_scratch_size.argtypes = [i, i, i, i, i]
+    L.attn_naive_scratch_size.restype = sz
+    L.attn_status_string.argtypes = [i]
+    L.attn_status_string.restype = ctypes.c_char_p
+    L.attn_version.argtypes = []
+    L.attn_version.restype = i
+    _lib = L
+    return L
+
+
+# ---- host-only queries ---------------------------------------------------------
+def attn_status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def attn_version() -> int:
+    return load_library().attn_version()
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    if dtype not in _DTYPE:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return _DTYPE[dtype]
+
+
+def attn_fwd_plan(B: int, H: int, Sq: int, Sk: int, d: int, dtype: torch.dtype) -> int:
+    n = ctypes.c_int(0)
+    rc = load_library().attn_fwd_plan(B, H, Sq, Sk, d, dtype_code(dtype), ctypes.byref(n))
+    if rc:
+        raise AttnError("attn_fwd_plan", rc)
+    return n.value
+
+
+def attn_fwd_workspace_size(B: int, H: int, Sq: int, Sk: int, d: int, dtype: torch.dtype) -> int:
+    return load_library().attn_fwd_workspace_size(B, H, Sq, Sk, d, dtype_code(dtype))
+
+
+def attn_splitk_workspace_size(B: int, H: int, Sq: int, d: int, n_split: int) -> int:
+    return load_library().attn_splitk_workspace_size(B, H, Sq, d, n_split)
+
+
+def attn_naive_scratch_size(B: int, H: int, Sq: int, Sk: int, dtype: torch.dtype) -> int:
+    return load_library().attn_naive_scratch_size(B, H, Sq, Sk, dtype_code(dtype))
+
+
+# ---- marshalling -----------------------------------------------------------------
+def dims(q: torch.Tensor, k: torch.Tensor, layout: str):
+    if layout == "bhsd":
+        B, H, Sq, d = q.shape
+        Sk = k.shape[2]
+    elif layout == "bshd":
+        B, Sq, H, d = q.shape
+        Sk = k.shape[1]
+    else:
+        raise ValueError(f"layout must be 'bhsd' or 'bshd', not {layout!r}")
+    return int(B), int(H), int(Sq), int(Sk), int(d)
+
+
+def _prepare(q, k, v, layout, kv_len, scale, lse, return_lse, out):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous in the {layout} layout")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if q.dim() != 4 or k.dim() != 4 or tuple(k.shape) != tuple(v.shape):
+        raise ValueError("q, k, v must be 4-D and k, v must have the same shape")
+    B, H, Sq, Sk, d = dims(q, k, layout)
+    kshape = (B, H, Sk, d) if layout == "bhsd" else (B, Sk, H, d)
+    if tuple(k.shape) != kshape:
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected {kshape}")
+    if kv_len is not None:
+        if kv_len.device != q.device or kv_len.dtype != torch.int32 or tuple(kv_len.shape) != (B,):
+            raise ValueError("kv_len must be an int32 tensor of shape [B] on q's device")
+        kv_len = kv_len.contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
+        raise ValueError("out must match q in shape, dtype and layout")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    return (B, H, Sq, Sk, d), kv_len, float(scale), o, lse
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(q, stream):
+    if stream is None:
+        return torch.cuda.current_stream(q.device).cuda_stream
+    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+
+
+def _scratch(nbytes, device, given):
+    if nbytes == 0:
+        return None
+    if given is not None:
+        return given
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def attn_fwd(q, k, v, *, scale=None, causal=False, layout="bhsd", kv_len=None, return_lse=True,
+             out=None, lse=None, workspace=None, stream=None):
+    """Fused forward. Returns (o, lse); lse is None when return_lse is False."""
+    (B, H, Sq, Sk, d), kv_len, scale, o, lse = _prepare(q, k, v, layout, kv_len, scale, lse,
+                                                        return_lse, out)
+    dt = dtype_code(q.dtype)
+    nbytes = attn_fwd_workspace_size(B, H, Sq, Sk, d, q.dtype)
+    ws = _scratch(nbytes, q.device, workspace)
+    rc = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq, Sk, d,
+                                 scale, int(bool(causal)), _LAYOUT[layout], dt, _ptr(kv_len),
+                                 _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                 _stream(q, stream))
+    if rc:
+        raise AttnError("attn_fwd", rc)
+    return o, lse
+
+
+def attn_fwd_splitk(q, k, v, *, n_split, scale=None, causal=False, layout="bhsd", kv_len=None,
+                    return_lse=True, out=None, lse=None, workspace=None, stream=None):
+    """Split-over-keys forward with an explicit split count. Returns (o, lse)."""
+    (B, H, Sq, Sk, d), kv_len, scale, o, lse = _prepare(q, k, v, layout, kv_len, scale, lse,
+                                                        return_lse, out)
+    nbytes = attn_splitk_workspace_size(B, H, Sq, d, int(n_split))
+    ws = _scratch(nbytes, q.device, workspace)
+    rc = load_library().attn_fwd_splitk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq,
+                                        Sk, d, scale, int(bool(causal)), _LAYOUT[layout],
+                                        dtype_code(q.dtype), _ptr(kv_len), int(n_split), _ptr(ws),
+                                        0 if ws is None else ws.numel() * ws.element_size(),
+                                        _stream(q, stream))
+    if rc:
+        raise AttnError("attn_fwd_splitk", rc)
+    return o, lse
+
+
+def attn_fwd_naive(q, k, v, *, scale=None, causal=False, layout="bhsd", kv_len=None,
+                   return_lse=True, out=None, lse=None, scratch=None, stream=None):
+    """Unfused three-kernel baseline (materialised S and P). Returns (o, lse)."""
+    (B, H, Sq, Sk, d), kv_len, scale, o, lse = _prepare(q, k, v, layout, kv_len, scale, lse,
+                                                        return_lse, out)
+    nbytes = attn_naive_scratch_size(B, H, Sq, Sk, q.dtype)
+    sc = _scratch(nbytes, q.device, scratch)
+    rc = load_library().attn_fwd_naive(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq,
+                                       Sk, d, scale, int(bool(causal)), _LAYOUT[layout],
+                                       dtype_code(q.dtype), _ptr(kv_len), _ptr(sc),
+                                       0 if sc is None else sc.numel() * sc.element_size(),
+                                       _stream(q, stream))
+    if rc:
+        raise AttnError("attn_fwd_naive", rc)
+    return o, lse

@@ -1,0 +1,170 @@
+// C ABI of libattn (declared in include/attn.h): argument validation, the
+// choice between the fused kernel and the split-over-keys pair, and launch.
+// Every check runs on the host before any HIP call, so a rejected call never
+// touches the GPU.
+#include "attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kPrefillRowsPerWorkgroup = 128;
+constexpr int kSplitMaxQueries = 4;     // query rows at which the split path can pay off
+constexpr int kSplitTargetGroups = 2048; // about 8 workgroups per compute unit
+constexpr int kSplitMinKeys = 512;      // keys per split, at least
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(int B, int H, int Sq, int Sk, int d, int layout, int dtype) {
+    if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return ATTN_E_SHAPE;
+    if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
+    if (layout != ATTN_LAYOUT_BHSD && layout != ATTN_LAYOUT_BSHD) return ATTN_E_UNSUPPORTED;
+    if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
+    // every row index (b*H + h)*S + s and every workgroup count fits in int32
+    const int64_t rows_q = (int64_t)B * H * Sq;
+    const int64_t rows_k = (int64_t)B * H * Sk;
+    if (rows_q > INT_MAX || rows_k > INT_MAX) return ATTN_E_SHAPE;
+    return ATTN_OK;
+}
+
+int check_call(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               int B, int H, int Sq, int Sk, int d, float scale, int layout, int dtype,
+               const int32_t* kv_len) {
+    if (!q || !k || !v || !o) return ATTN_E_NULLPTR;
+    int rc = check_shape(B, H, Sq, Sk, d, layout, dtype);
+    if (rc != ATTN_OK) return rc;
+    if (!std::isfinite(scale) || scale < 0.f) return ATTN_E_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return ATTN_E_ALIGN;
+    if (!aligned(lse, 4) || !aligned(kv_len, 4)) return ATTN_E_ALIGN;
+    return ATTN_OK;
+}
+
+int plan_splits(int B, int H, int Sq, int Sk) {
+    if (Sq > kSplitMaxQueries) return 1;
+    const int64_t prefill_groups = (int64_t)((Sq + kPrefillRowsPerWorkgroup - 1) / kPrefillRowsPerWorkgroup) * B * H;
+    if (prefill_groups >= kSplitTargetGroups / 4) return 1;
+    const int64_t rows = (int64_t)B * H * Sq;
+    int64_t n = (kSplitTargetGroups + rows - 1) / rows;
+    const int64_t max_by_keys = Sk / kSplitMinKeys;
+    if (n > max_by_keys) n = max_by_keys;
+    if (n > 256) n = 256;
+    return n < 2 ? 1 : (int)n;
+}
+
+attn::FwdArgs make_args(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
+                        int dtype, const int32_t* kv_len) {
+    attn::FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.kv_len = kv_len;
+    a.B = B;
+    a.H = H;
+    a.Sq = Sq;
+    a.Sk = Sk;
+    a.d = d;
+    a.scale = scale;
+    a.causal = causal != 0;
+    a.layout = layout;
+    a.dtype = dtype;
+    return a;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_plan(int B, int H, int Sq, int Sk, int d, int dtype, int* n_split) {
+    if (!n_split) return ATTN_E_NULLPTR;
+    int rc = check_shape(B, H, Sq, Sk, d, ATTN_LAYOUT_BHSD, dtype);
+    if (rc != ATTN_OK) return rc;
+    *n_split = plan_splits(B, H, Sq, Sk);
+    return ATTN_OK;
+}
+
+size_t attn_splitk_workspace_size(int B, int H, int Sq, int d, int n_split) {
+    if (n_split < 1 || check_shape(B, H, Sq, 1, d, ATTN_LAYOUT_BHSD, ATTN_F32) != ATTN_OK) return 0;
+    return attn::splitk_workspace_bytes(B, H, Sq, d, n_split);
+}
+
+size_t attn_fwd_workspace_size(int B, int H, int Sq, int Sk, int d, int dtype) {
+    if (check_shape(B, H, Sq, Sk, d, ATTN_LAYOUT_BHSD, dtype) != ATTN_OK) return 0;
+    const int n = plan_splits(B, H, Sq, Sk);
+    return n > 1 ? attn::splitk_workspace_bytes(B, H, Sq, d, n) : 0;
+}
+
+int attn_fwd_splitk(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
+                    int dtype, const int32_t* kv_len, int n_split, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    int rc = check_call(q, k, v, o, lse, B, H, Sq, Sk, d, scale, layout, dtype, kv_len);
+    if (rc != ATTN_OK) return rc;
+    if (n_split < 1 || (int64_t)B * H * Sq * n_split > INT_MAX) return ATTN_E_SHAPE;
+    const size_t need = attn::splitk_workspace_bytes(B, H, Sq, d, n_split);
+    if (!workspace || workspace_bytes < need) return ATTN_E_WORKSPACE;
+    if (!aligned(workspace, 16)) return ATTN_E_ALIGN;
+    const attn::FwdArgs a = make_args(q, k, v, o, lse, B, H, Sq, Sk, d, scale, causal, layout, dtype, kv_len);
+    return status_of(attn::run_splitk(a, n_split, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
+             int dtype, const int32_t* kv_len, void* workspace, size_t workspace_bytes,
+             void* stream) {
+    int rc = check_call(q, k, v, o, lse, B, H, Sq, Sk, d, scale, layout, dtype, kv_len);
+    if (rc != ATTN_OK) return rc;
+    const int n = plan_splits(B, H, Sq, Sk);
+    if (n > 1)
+        return attn_fwd_splitk(q, k, v, o, lse, B, H, Sq, Sk, d, scale, causal, layout, dtype, kv_len, n,
+                               workspace, workspace_bytes, stream);
+    const attn::FwdArgs a = make_args(q, k, v, o, lse, B, H, Sq, Sk, d, scale, causal, layout, dtype, kv_len);
+    return status_of(attn::run_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t attn_naive_scratch_size(int B, int H, int Sq, int Sk, int dtype) {
+    if (check_shape(B, H, Sq, Sk, 64, ATTN_LAYOUT_BHSD, dtype) != ATTN_OK) return 0;
+    return attn::naive_scratch_bytes(B, H, Sq, Sk, dtype);
+}
+
+int attn_fwd_naive(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
+                   int dtype, const int32_t* kv_len, void* scratch, size_t scratch_bytes,
+                   void* stream) {
+    int rc = check_call(q, k, v, o, lse, B, H, Sq, Sk, d, scale, layout, dtype, kv_len);
+    if (rc != ATTN_OK) return rc;
+    const size_t need = attn::naive_scratch_bytes(B, H, Sq, Sk, dtype);
+    if (!scratch || scratch_bytes < need) return ATTN_E_WORKSPACE;
+    if (!aligned(scratch, 16)) return ATTN_E_ALIGN;
+    const attn::FwdArgs a = make_args(q, k, v, o, lse, B, H, Sq, Sk, d, scale, causal, layout, dtype, kv_len);
+    return status_of(attn::run_naive(a, scratch, static_cast<hipStream_t>(stream)));
+}
+
+const char* attn_status_string(int status) {
+    switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_NULLPTR: return "a required pointer is NULL";
+    case ATTN_E_SHAPE: return "invalid shape: B, H, Sq, Sk and n_split must be >= 1 and sizes must fit";
+    case ATTN_E_UNSUPPORTED: return "unsupported head size (64 or 128), layout or dtype";
+    case ATTN_E_ALIGN: return "misaligned pointer (tensors and workspaces 16 bytes, lse and kv_len 4 bytes)";
+    case ATTN_E_WORKSPACE: return "workspace or scratch missing or too small";
+    case ATTN_E_HIP: return "the HIP runtime reported an error at launch";
+    case ATTN_E_ARG: return "scale must be finite and >= 0";
+    default: return "unknown status";
+    }
+}
+
+int attn_version(void) { return kVersion; }
+
+}  // extern "C"

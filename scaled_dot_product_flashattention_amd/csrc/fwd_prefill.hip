@@ -1,0 +1,408 @@
+// Fused attention forward: one kernel, scores and probabilities stay on chip.
+//
+// Method (chapter "2. 自注意力机制算子…以及FlashAttention优化", §2.6, and the
+// section "FlashAttention 分块计算原理与浏览器适配" of the WebGPU page): the
+// queries of one head are cut into tiles of BM rows, the keys/values into
+// tiles of BN rows. A workgroup owns one query tile, streams every key/value
+// tile it needs through LDS, and keeps per query row a running maximum m and a
+// running sum l; when a new tile raises m, the sum and the partial output are
+// first multiplied by exp(m_old - m_new). The output is divided by l once, at
+// the end.
+//
+// Mapping to gfx950:
+//   * 4 waves per workgroup, each owning 32*NQ query rows; BM = 128*NQ.
+//   * Scores are computed transposed, S^T = K Q^T, with 32x32 matrix-core
+//     blocks: a lane then owns one query (its column) and 32 of the 64 keys
+//     of a tile (its rows), so the row max and row sum are in-lane except for
+//     one exchange between the two lane halves.
+//   * The output is kept transposed too, O^T += V^T P^T: the probabilities
+//     feed the second product straight from the score registers, and the
+//     rescale by exp(m_old - m_new) touches only the lane's own query.
+//   * K tiles sit in LDS row-major; V tiles are transposed while being stored
+//     to LDS so both operands are read as contiguous vectors. Both are double
+//     buffered: tile t+1 is fetched into registers while tile t is computed.
+//   * Workgroups of one head are kept on one XCD (its L2 then serves every
+//     re-read of that head's K/V); causal tiles are started longest-first.
+//   * Exponentials are base 2 with scale*log2(e) folded into one FMA.
+#include "device_common.h"
+#include "launch.h"
+
+namespace attn {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+
+struct PrefillParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    const int32_t* kv_len;
+    Strides sq;  // q and o
+    Strides sk;  // k and v
+    int B, H, Sq, Sk;
+    float c;  // scale * log2(e)
+    int causal;
+    int n_qtiles;
+    int remap;  // grid size is a multiple of 8: group each head's tiles on one XCD
+};
+
+template <typename Tag, int D, int NQ>
+struct PrefillCfg {
+    static constexpr int NW = 4;                 // waves per workgroup
+    static constexpr int BM = NW * 32 * NQ;      // query rows per workgroup
+    static constexpr int BN = 64;                // keys per tile
+    static constexpr int ES = Tag::bytes;        // element bytes
+    static constexpr int KROW = D + 16 / ES;     // LDS K row, padded by 16 B
+    static constexpr int VROW = BN + 8 / ES;     // LDS V^T row, padded by 8 B
+    static constexpr int K_ELEMS = BN * KROW;
+    static constexpr int V_ELEMS = D * VROW;
+    static constexpr int STAGE_BYTES = (K_ELEMS + V_ELEMS) * ES;
+    static constexpr int OROW = D + 16 / ES;     // output staging row
+    static constexpr int OUT_BYTES = NW * 32 * NQ * OROW * ES;
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES > OUT_BYTES ? 2 * STAGE_BYTES : OUT_BYTES;
+    static constexpr int EPC = 16 / ES;          // elements per 16-byte chunk
+    static constexpr int CPR = D / EPC;          // 16-byte chunks per row
+    static constexpr int KCH = BN * CPR / 256;   // K chunks per thread and tile
+    static_assert(BN * CPR % 256 == 0, "tile must split evenly over 256 threads");
+};
+
+template <typename Tag, int D, int NQ>
+__global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(PrefillParams p) {
+    using C = PrefillCfg<Tag, D, NQ>;
+    using T = typename Tag::storage;
+    constexpr int BN = C::BN;
+    constexpr bool k16 = (C::ES == 2);
+
+    __shared__ __align__(16) unsigned char smem[C::LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int n32 = lane & 31;
+    const int hh = lane >> 5;
+
+    // ---- which (batch, head, query tile) ---------------------------------
+    const int G = gridDim.x;
+    const int g = blockIdx.x;
+    const int w = p.remap ? (g & 7) * (G >> 3) + (g >> 3) : g;
+    const int bh = w / p.n_qtiles;
+    int qt = w - bh * p.n_qtiles;
+    if (p.causal) qt = p.n_qtiles - 1 - qt;  // longest causal tiles first
+    const int b = bh / p.H;
+    const int h = bh - b * p.H;
+
+    const int nb = clamp_len(p.kv_len, b, p.Sk);
+    const int q0 = qt * C::BM;
+    const int q_end = min(q0 + C::BM, p.Sq);
+    const int kend = p.causal ? min(nb, q_end) : nb;  // keys any row of the tile can see
+    const int ntiles = (kend + BN - 1) / BN;
+
+    const T* qp = static_cast<const T*>(p.q) + b * p.sq.b + h * p.sq.h;
+    const T* kp = static_cast<const T*>(p.k) + b * p.sk.b + h * p.sk.h;
+    const T* vp = static_cast<const T*>(p.v) + b * p.sk.b + h * p.sk.h;
+    T* op = static_cast<T*>(p.o) + b * p.sq.b + h * p.sq.h;
+
+    const int qw0 = q0 + wave * 32 * NQ;  // first query row of this wave
+    const bool wave_active = qw0 < p.Sq;
+    const int wave_kend = p.causal ? min(nb, min(qw0 + 32 * NQ, p.Sq)) : nb;
+    const int wave_lim_min = p.causal ? min(nb, qw0 + 1) : nb;  // tiles past this need masks
+
+    // ---- Q operands, held in registers for the whole key loop -------------
+    // 16-bit: B operand of S^T = K Q^T, K-step s holds q[row][16s + 8h .. +7].
+    // fp32:   K-step s holds q[row][2s + h].
+    constexpr int QSTEPS = k16 ? D / 16 : D / 2;
+    typedef typename std::conditional<k16, u32x4, float>::type QOp;
+    QOp qop[NQ][QSTEPS];
+#pragma unroll
+    for (int gq = 0; gq < NQ; ++gq) {
+        const int qi = qw0 + gq * 32 + n32;
+        const bool ok = qi < p.Sq;
+        const T* row = qp + (int64_t)(ok ? qi : 0) * p.sq.s;
+#pragma unroll
+        for (int s = 0; s < QSTEPS; ++s) {
+            if constexpr (k16) {
+                u32x4 z = {0u, 0u, 0u, 0u};
+                qop[gq][s] = ok ? *reinterpret_cast<const u32x4*>(row + s * 16 + hh * 8) : z;
+            } else {
+                qop[gq][s] = ok ? row[2 * s + hh] : 0.f;
+            }
+        }
+    }
+
+    // ---- global -> register -> LDS staging of one K/V tile -----------------
+    // K: 16-byte chunks, consecutive threads along a row (coalesced).
+    // V (16-bit): pairs of key rows, so the transposed LDS store writes two
+    //   keys (one 32-bit word) per d; V (fp32): single elements.
+    constexpr int VCH = k16 ? (BN / 2) * C::CPR / 256 : BN * C::CPR / 256;
+    constexpr int VREGS = k16 ? 2 : 1;
+    static_assert(VCH >= 1, "V tile must cover all threads");
+    u32x4 kreg[C::KCH];
+    u32x4 vreg[VCH][VREGS];
+
+    auto load_tile = [&](int t) {
+        const int key0 = t * BN;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < C::KCH; ++c) {
+            const int idx = tid + c * 256;
+            const int row = idx / C::CPR, cc = idx - row * C::CPR;
+            const int key = key0 + row;
+            kreg[c] = key < nb ? *reinterpret_cast<const u32x4*>(kp + (int64_t)key * p.sk.s + cc * C::EPC) : z;
+        }
+#pragma unroll
+        for (int c = 0; c < VCH; ++c) {
+            const int idx = tid + c * 256;
+            const int pr = idx / C::CPR, cc = idx - pr * C::CPR;
+#pragma unroll
+            for (int e = 0; e < VREGS; ++e) {
+                const int key = key0 + pr * VREGS + e;
+                vreg[c][e] = key < nb ? *reinterpret_cast<const u32x4*>(vp + (int64_t)key * p.sk.s + cc * C::EPC) : z;
+            }
+        }
+    };
+
+    auto store_tile = [&](int buf) {
+        T* Ks = reinterpret_cast<T*>(smem + buf * C::STAGE_BYTES);
+        T* Vt = Ks + C::K_ELEMS;
+#pragma unroll
+        for (int c = 0; c < C::KCH; ++c) {
+            const int idx = tid + c * 256;
+            const int row = idx / C::CPR, cc = idx - row * C::CPR;
+            *reinterpret_cast<u32x4*>(Ks + row * C::KROW + cc * C::EPC) = kreg[c];
+        }
+#pragma unroll
+        for (int c = 0; c < VCH; ++c) {
+            const int idx = tid + c * 256;
+            const int pr = idx / C::CPR, cc = idx - pr * C::CPR;
+            if constexpr (k16) {
+                // vreg[c][0] = V[2pr][8cc .. +7], vreg[c][1] = V[2pr+1][8cc .. +7]
+                store_pair_transposed(Vt, C::VROW, cc, pr, vreg[c][0], vreg[c][1]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    reinterpret_cast<uint32_t*>(Vt)[(cc * 4 + e) * C::VROW + pr] = vreg[c][0][e];
+            }
+        }
+    };
+
+    // ---- running state -----------------------------------------------------
+    f32x16 oacc[NQ][D / 32];
+    float m_run[NQ], l_run[NQ];
+#pragma unroll
+    for (int gq = 0; gq < NQ; ++gq) {
+        m_run[gq] = kNegInf;
+        l_run[gq] = 0.f;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[gq][db][r] = 0.f;
+    }
+    const float c = p.c;
+
+    if (ntiles > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < ntiles) load_tile(t + 1);
+
+        if (wave_active && t * BN < wave_kend) {
+            const T* Ks = reinterpret_cast<const T*>(smem + buf * C::STAGE_BYTES);
+            const T* Vt = Ks + C::K_ELEMS;
+
+            // -- scores S^T (keys x queries), 2 key blocks of 32 -------------
+            f32x16 sacc[BN / 32][NQ];
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                for (int gq = 0; gq < NQ; ++gq)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sacc[kb][gq][r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < QSTEPS; ++s) {
+#pragma unroll
+                for (int kb = 0; kb < BN / 32; ++kb) {
+                    const T* krow = Ks + (kb * 32 + n32) * C::KROW;
+                    if constexpr (k16) {
+                        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + s * 16 + hh * 8);
+#pragma unroll
+                        for (int gq = 0; gq < NQ; ++gq) sacc[kb][gq] = mfma16<Tag>(a, qop[gq][s], sacc[kb][gq]);
+                    } else {
+                        const float a = krow[2 * s + hh];
+#pragma unroll
+                        for (int gq = 0; gq < NQ; ++gq) sacc[kb][gq] = mfma_f32(a, qop[gq][s], sacc[kb][gq]);
+                    }
+                }
+            }
+
+            // -- online softmax update, one query per lane and group ---------
+            const bool need_mask = (t + 1) * BN > wave_lim_min;
+#pragma unroll
+            for (int gq = 0; gq < NQ; ++gq) {
+                const int qi = qw0 + gq * 32 + n32;
+                const int lim = p.causal ? min(nb, qi + 1) : nb;
+                float mx = kNegInf;
+                if (need_mask) {
+#pragma unroll
+                    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int j = t * BN + kb * 32 + blk_row(r, hh);
+                            if (j >= lim) sacc[kb][gq][r] = kNegInf;
+                        }
+                }
+#pragma unroll
+                for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][gq][r]);
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float mxs = (mx == kNegInf) ? kNegInf : mx * c;
+                const float m_new = fmaxf(m_run[gq], mxs);
+                const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+                const float alpha = fast_exp2(m_run[gq] - m_use);
+                m_run[gq] = m_new;
+                float rs = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float x = sacc[kb][gq][r];
+                        float pr = fast_exp2(fmaf(x, c, -m_use));
+                        if (need_mask) pr = (x == kNegInf) ? 0.f : pr;
+                        sacc[kb][gq][r] = pr;
+                        rs += pr;
+                    }
+                l_run[gq] = l_run[gq] * alpha + rs;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[gq][db][r] *= alpha;
+            }
+
+            // -- O^T += V^T P^T ------------------------------------------------
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb) {
+                if constexpr (k16) {
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        u32x4 pop[NQ];
+#pragma unroll
+                        for (int gq = 0; gq < NQ; ++gq) {
+                            const f32x16& sv = sacc[kb][gq];
+                            pop[gq] = u32x4{pack2<Tag>(sv[8 * u + 0], sv[8 * u + 1]),
+                                            pack2<Tag>(sv[8 * u + 2], sv[8 * u + 3]),
+                                            pack2<Tag>(sv[8 * u + 4], sv[8 * u + 5]),
+                                            pack2<Tag>(sv[8 * u + 6], sv[8 * u + 7])};
+                        }
+#pragma unroll
+                        for (int db = 0; db < D / 32; ++db) {
+                            const T* vrow = Vt + (db * 32 + n32) * C::VROW + kb * 32 + 16 * u + 4 * hh;
+                            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+                            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+                            const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                            for (int gq = 0; gq < NQ; ++gq) oacc[gq][db] = mfma16<Tag>(a, pop[gq], oacc[gq][db]);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+                        for (int db = 0; db < D / 32; ++db) {
+                            const float a = Vt[(db * 32 + n32) * C::VROW + kb * 32 + blk_row(r, hh)];
+#pragma unroll
+                            for (int gq = 0; gq < NQ; ++gq) oacc[gq][db] = mfma_f32(a, sacc[kb][gq][r], oacc[gq][db]);
+                        }
+                    }
+                }
+            }
+        }
+
+        if (t + 1 < ntiles) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2 -------------------
+    T* Os = reinterpret_cast<T*>(smem) + wave * 32 * NQ * C::OROW;
+#pragma unroll
+    for (int gq = 0; gq < NQ; ++gq) {
+        const float lt = l_run[gq] + __shfl_xor(l_run[gq], 32);
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const int qi = qw0 + gq * 32 + n32;
+        if (hh == 0 && p.lse != nullptr && qi < p.Sq)
+            p.lse[((int64_t)b * p.H + h) * p.Sq + qi] = lt > 0.f ? (m_run[gq] + log2f(lt)) * kLn2 : kNegInf;
+        T* orow = Os + (gq * 32 + n32) * C::OROW;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int d0 = db * 32 + 8 * jj + 4 * hh;
+                const f32x16& ov = oacc[gq][db];
+                if constexpr (k16) {
+                    const u32x2 pk = {pack2<Tag>(ov[4 * jj] * inv, ov[4 * jj + 1] * inv),
+                                      pack2<Tag>(ov[4 * jj + 2] * inv, ov[4 * jj + 3] * inv)};
+                    *reinterpret_cast<u32x2*>(orow + d0) = pk;
+                } else {
+                    const f32x4 pk = {ov[4 * jj] * inv, ov[4 * jj + 1] * inv, ov[4 * jj + 2] * inv,
+                                      ov[4 * jj + 3] * inv};
+                    *reinterpret_cast<f32x4*>(orow + d0) = pk;
+                }
+            }
+    }
+    __syncthreads();
+    // coalesced copy of the wave's rows to global memory
+    for (int cidx = lane; cidx < 32 * NQ * C::CPR; cidx += 64) {
+        const int row = cidx / C::CPR, cc = cidx - row * C::CPR;
+        const int qi = qw0 + row;
+        if (qi < p.Sq)
+            *reinterpret_cast<u32x4*>(op + (int64_t)qi * p.sq.s + cc * C::EPC) =
+                *reinterpret_cast<const u32x4*>(Os + row * C::OROW + cc * C::EPC);
+    }
+}
+
+template <typename Tag, int D, int NQ>
+hipError_t launch_prefill(const FwdArgs& a, hipStream_t stream) {
+    using C = PrefillCfg<Tag, D, NQ>;
+    PrefillParams p;
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.o = a.o;
+    p.lse = a.lse;
+    p.kv_len = a.kv_len;
+    p.sq = make_strides(a.layout, a.H, a.Sq, a.d);
+    p.sk = make_strides(a.layout, a.H, a.Sk, a.d);
+    p.B = a.B;
+    p.H = a.H;
+    p.Sq = a.Sq;
+    p.Sk = a.Sk;
+    p.c = a.scale * kLog2e;
+    p.causal = a.causal ? 1 : 0;
+    p.n_qtiles = (a.Sq + C::BM - 1) / C::BM;
+    const int64_t grid = (int64_t)p.n_qtiles * a.B * a.H;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    p.remap = (grid % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((fwd_prefill_kernel<Tag, D, NQ>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t run_prefill(const FwdArgs& a, hipStream_t stream) {
+    switch (a.dtype) {
+    case 2:
+        return a.d == 64 ? launch_prefill<BF16, 64, 1>(a, stream) : launch_prefill<BF16, 128, 1>(a, stream);
+    case 1:
+        return a.d == 64 ? launch_prefill<F16, 64, 1>(a, stream) : launch_prefill<F16, 128, 1>(a, stream);
+    default:
+        return a.d == 64 ? launch_prefill<F32, 64, 1>(a, stream) : launch_prefill<F32, 128, 1>(a, stream);
+    }
+}
+
+}  // namespace attn

@@ -1,0 +1,36 @@
+// Host-side launchers of the libattn kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Arguments of one forward call after validation (see include/attn.h).
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    const int32_t* kv_len;
+    int B, H, Sq, Sk, d;
+    float scale;
+    int causal;
+    int layout;  // 0 = [B,H,S,d], 1 = [B,S,H,d]
+    int dtype;   // 0 = fp32, 1 = fp16, 2 = bf16
+};
+
+// Fused single-kernel forward (any shape).
+hipError_t run_prefill(const FwdArgs& a, hipStream_t stream);
+
+// Split-over-keys forward: partial kernel + merge kernel.
+size_t splitk_workspace_bytes(int B, int H, int Sq, int d, int n_split);
+hipError_t run_splitk(const FwdArgs& a, int n_split, void* workspace, hipStream_t stream);
+
+// Unfused three-kernel baseline.
+size_t naive_scratch_bytes(int B, int H, int Sq, int Sk, int dtype);
+hipError_t run_naive(const FwdArgs& a, void* scratch, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,127 @@
+"""Shared helpers of the GPU parity tests: run a path of libattn on seeded
+inputs and compare it with the fp64 oracle, element by element.
+
+Tolerances (the study's stated bar):
+  * bf16 / fp16 inputs: max |O_gpu - O_oracle| <= 2e-2 over every element,
+    and the same absolute bound on LSE;
+  * fp32 inputs: max |O_gpu - O_oracle| <= 1e-5 * max |O_oracle| (normwise
+    relative; elementwise relative error is undefined near O = 0), and the
+    same rule for LSE.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import scaled_dot_product_flashattention_amd as sdpa
+from scaled_dot_product_flashattention_amd.inputs import Workload, generate, poison_padding
+
+TOL_16 = 2e-2
+TOL_32_REL = 1e-5
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(t):
+    return None if t is None else t.cuda()
+
+
+def run_path(path, q, k, v, w: Workload, kv_len, n_split=None, scale=None):
+    kw = dict(scale=w.scale if scale is None else scale, causal=w.causal, layout=w.layout,
+              kv_len=kv_len)
+    if path == "fused":
+        return sdpa.attn_fwd(q, k, v, **kw)
+    if path == "splitk":
+        return sdpa.attn_fwd_splitk(q, k, v, n_split=n_split, **kw)
+    if path == "naive":
+        return sdpa.attn_fwd_naive(q, k, v, **kw)
+    raise ValueError(path)
+
+
+def errors(o_gpu, lse_gpu, o_ref, lse_ref):
+    o = o_gpu.float().cpu().numpy().astype(np.float64)
+    l = lse_gpu.cpu().numpy().astype(np.float64)
+    both_inf = np.isneginf(l) & np.isneginf(lse_ref)
+    with np.errstate(invalid="ignore"):
+        dl = np.where(both_inf, 0.0, np.abs(l - lse_ref))
+    return np.abs(o - o_ref), dl
+
+
+def check(w: Workload, o_err, l_err, o_ref, lse_ref, what=""):
+    assert not np.isnan(o_err).any(), f"{what}: NaN in the output"
+    assert not np.isnan(l_err).any(), f"{what}: NaN/inf mismatch in LSE"
+    eo = float(o_err.max()) if o_err.size else 0.0
+    el = float(l_err.max()) if l_err.size else 0.0
+    if w.dtype == "f32":
+        bo = TOL_32_REL * max(float(np.abs(o_ref).max()), 1e-30)
+        fin = np.isfinite(lse_ref)
+        bl = TOL_32_REL * max(float(np.abs(lse_ref[fin]).max()) if fin.any() else 0.0, 1e-30)
+    else:
+        bo = bl = TOL_16
+    say(f"  {what}: max|dO| = {eo:.3e} (bound {bo:.1e}), max|dLSE| = {el:.3e} (bound {bl:.1e})")
+    assert eo <= bo, f"{what}: max|dO| {eo:.3e} > {bo:.1e}"
+    assert el <= bl, f"{what}: max|dLSE| {el:.3e} > {bl:.1e}"
+    return eo, el
+
+
+def full_case(w: Workload, path="fused", n_split=None, poison=False, seed=None, scale=None):
+    """Whole-output comparison; the oracle computes every row."""
+    say(f"case {w.name} {path} n_split={n_split} B{w.B} H{w.H} Sq{w.Sq} Sk{w.Sk} d{w.d} "
+        f"{w.dtype} {w.layout} causal={w.causal} pad={w.kv_len_range}")
+    t = generate(w, seed)
+    if poison:
+        poison_padding(t["k"], t["v"], t["kv_len"], w.layout)
+    sc = w.scale if scale is None else scale
+    o_ref, lse_ref = oracle.attention(t["q"], t["k"], t["v"], scale=sc, causal=w.causal,
+                                      layout=w.layout, kv_len=t["kv_len"])
+    q, k, v, kl = (to_dev(t[n]) for n in ("q", "k", "v", "kv_len"))
+    o, lse = run_path(path, q, k, v, w, kl, n_split, scale=sc)
+    torch.cuda.synchronize()
+    oe, le = errors(o, lse, o_ref, lse_ref)
+    return check(w, oe, le, o_ref, lse_ref, f"{w.name}/{path}")
+
+
+def sampled_rows(w: Workload, n: int, rng) -> np.ndarray:
+    """Rows (b*H + h)*Sq + i to check at full size: first and last rows, tile
+    edges, the ragged end, and random picks."""
+    R = w.B * w.H * w.Sq
+    picks = {0, R - 1, w.Sq - 1, min(w.Sq, 127), min(w.Sq - 1, 128), (w.B - 1) * w.H * w.Sq}
+    picks |= set(rng.choice(R, size=min(n, R), replace=False).tolist())
+    return np.array(sorted(p for p in picks if 0 <= p < R), dtype=np.int64)
+
+
+def sampled_case(w: Workload, path="fused", n_rows=48, n_split=None, seed=None):
+    """Full-size run on the GPU; the oracle recomputes sampled rows."""
+    say(f"case {w.name} full size {path} B{w.B} H{w.H} Sq{w.Sq} Sk{w.Sk} d{w.d} {w.dtype} "
+        f"{w.layout} causal={w.causal}")
+    t = generate(w, seed)
+    q, k, v, kl = (to_dev(t[n]) for n in ("q", "k", "v", "kv_len"))
+    o, lse = run_path(path, q, k, v, w, kl, n_split)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1234)
+    rows = sampled_rows(w, n_rows, rng)
+    o_ref, lse_ref = oracle.attention_rows(t["q"], t["k"], t["v"], rows, scale=w.scale,
+                                           causal=w.causal, layout=w.layout, kv_len=t["kv_len"])
+    o_c = o.float().cpu()
+    lse_c = lse.cpu().numpy().astype(np.float64)
+    got = np.empty_like(o_ref)
+    got_l = np.empty_like(lse_ref)
+    for n, r in enumerate(rows):
+        i, h, b = r % w.Sq, (r // w.Sq) % w.H, r // (w.Sq * w.H)
+        got[n] = (o_c[b, h, i] if w.layout == "bhsd" else o_c[b, i, h]).numpy()
+        got_l[n] = lse_c[b, h, i]
+    both_inf = np.isneginf(got_l) & np.isneginf(lse_ref)
+    with np.errstate(invalid="ignore"):
+        dl = np.where(both_inf, 0.0, np.abs(got_l - lse_ref))
+    res = check(w, np.abs(got - o_ref), dl, o_ref, lse_ref, f"{w.name}/{path}/sampled")
+    # properties that hold at any size: finite output, |O| bounded by max|V|
+    assert torch.isfinite(o_c).all(), "non-finite output"
+    vmax = float(t["v"].float().abs().max())
+    assert float(o_c.abs().max()) <= vmax * (1 + 1e-2) + 1e-6, "|O| exceeds max |V|"
+    return res

@@ -1,0 +1,141 @@
+"""libattn's C ABI on the CPU: the library loads, exports every function that
+include/attn.h declares, and rejects bad arguments with the documented status
+before any HIP call. No call here reaches a kernel launch: every call either
+fails validation or is a host-only size/plan query."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import scaled_dot_product_flashattention_amd as sdpa
+from scaled_dot_product_flashattention_amd import build as attn_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, E_NULLPTR, E_SHAPE, E_UNSUPPORTED, E_ALIGN, E_WORKSPACE, E_HIP, E_ARG = range(8)
+BHSD, BSHD = 0, 1
+F32, F16, BF16 = 0, 1, 2
+
+# fake, never dereferenced device addresses (validation fails before any use)
+A16 = 0x10000
+A16_2 = 0x20000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(attn_build.library_path()):
+        attn_build.build()
+    return sdpa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"attn_fwd", "attn_fwd_splitk", "attn_fwd_naive", "attn_fwd_plan",
+            "attn_fwd_workspace_size", "attn_splitk_workspace_size", "attn_naive_scratch_size",
+            "attn_status_string", "attn_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"libattn.so does not export {n}"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.attn_version() >= 10000
+    seen = set()
+    for s in range(8):
+        txt = sdpa.attn_status_string(s)
+        assert txt and txt not in seen
+        seen.add(txt)
+    assert sdpa.attn_status_string(99) == "unknown status"
+
+
+def call(lib, fn="attn_fwd", q=A16, k=A16, v=A16, o=A16_2, lse=None, B=1, H=2, Sq=128, Sk=128,
+         d=64, scale=0.125, causal=0, layout=BHSD, dtype=BF16, kv_len=None, extra=None):
+    args = [q, k, v, o, lse, B, H, Sq, Sk, d, scale, causal, layout, dtype, kv_len]
+    if fn == "attn_fwd_splitk":
+        args += extra if extra is not None else [4, None, 0]
+    else:
+        args += extra if extra is not None else [None, 0]
+    return getattr(lib, fn)(*args, None)
+
+
+@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_splitk", "attn_fwd_naive"])
+def test_validation_statuses(lib, fn):
+    assert call(lib, fn, q=None) == E_NULLPTR
+    assert call(lib, fn, k=None) == E_NULLPTR
+    assert call(lib, fn, v=None) == E_NULLPTR
+    assert call(lib, fn, o=None) == E_NULLPTR
+    for bad in (dict(B=0), dict(H=0), dict(Sq=0), dict(Sk=0), dict(B=-3),
+                dict(B=1 << 16, H=1 << 10, Sq=1 << 10)):
+        assert call(lib, fn, **bad) == E_SHAPE, bad
+    for bad in (dict(d=96), dict(d=256), dict(d=0), dict(layout=2), dict(layout=-1),
+                dict(dtype=3), dict(dtype=-1)):
+        assert call(lib, fn, **bad) == E_UNSUPPORTED, bad
+    for bad in (float("nan"), float("inf"), float("-inf"), -0.5):
+        assert call(lib, fn, scale=bad) == E_ARG, bad
+    assert call(lib, fn, q=A16 + 8) == E_ALIGN
+    assert call(lib, fn, o=A16_2 + 2) == E_ALIGN
+    assert call(lib, fn, lse=A16 + 2) == E_ALIGN
+    assert call(lib, fn, kv_len=A16 + 1) == E_ALIGN
+
+
+def test_workspace_statuses(lib):
+    # decode shape: the plan splits, so attn_fwd needs a workspace
+    shape = dict(B=8, H=32, Sq=1, Sk=32768, d=128)
+    n = ctypes.c_int(0)
+    assert lib.attn_fwd_plan(8, 32, 1, 32768, 128, BF16, ctypes.byref(n)) == OK
+    assert n.value > 1
+    need = lib.attn_fwd_workspace_size(8, 32, 1, 32768, 128, BF16)
+    assert need == 8 * 32 * 1 * n.value * (128 + 4) * 4
+    assert call(lib, **shape, extra=[None, 0]) == E_WORKSPACE
+    assert call(lib, **shape, extra=[A16, need - 1]) == E_WORKSPACE
+    assert call(lib, **shape, extra=[A16 + 4, need]) == E_ALIGN
+    # explicit split count
+    assert call(lib, "attn_fwd_splitk", extra=[0, A16, 1 << 30]) == E_SHAPE
+    assert call(lib, "attn_fwd_splitk", extra=[4, None, 0]) == E_WORKSPACE
+    need4 = lib.attn_splitk_workspace_size(1, 2, 128, 64, 4)
+    assert need4 == 1 * 2 * 128 * 4 * (64 + 4) * 4
+    assert call(lib, "attn_fwd_splitk", extra=[4, A16, need4 - 4]) == E_WORKSPACE
+    # naive scratch: fp32 S plus P in the input type, rows padded to 64 keys
+    need_n = lib.attn_naive_scratch_size(1, 2, 128, 100, BF16)
+    assert need_n == 1 * 2 * 128 * 128 * (4 + 2)
+    assert lib.attn_naive_scratch_size(1, 2, 128, 100, F32) == 1 * 2 * 128 * 128 * 8
+    assert call(lib, "attn_fwd_naive", Sk=100, extra=[None, 0]) == E_WORKSPACE
+    assert call(lib, "attn_fwd_naive", Sk=100, extra=[A16, need_n - 1]) == E_WORKSPACE
+    assert call(lib, "attn_fwd_naive", Sk=100, extra=[A16 + 8, need_n]) == E_ALIGN
+
+
+def test_plan_and_size_queries(lib):
+    n = ctypes.c_int(-1)
+    # prefill shapes never split and need no workspace
+    for shp in ((1, 16, 4096, 4096, 64), (2, 16, 8192, 8192, 128), (32, 12, 512, 512, 64),
+                (1, 2, 256, 256, 64)):
+        assert lib.attn_fwd_plan(*shp, BF16, ctypes.byref(n)) == OK and n.value == 1
+        assert lib.attn_fwd_workspace_size(*shp, BF16) == 0
+    # single query over many keys splits; few keys do not
+    assert lib.attn_fwd_plan(8, 32, 1, 32768, 128, BF16, ctypes.byref(n)) == OK and n.value == 8
+    assert lib.attn_fwd_plan(1, 1, 1, 100, 64, BF16, ctypes.byref(n)) == OK and n.value == 1
+    # rejected arguments
+    assert lib.attn_fwd_plan(0, 1, 1, 1, 64, BF16, ctypes.byref(n)) == E_SHAPE
+    assert lib.attn_fwd_plan(1, 1, 1, 1, 80, BF16, ctypes.byref(n)) == E_UNSUPPORTED
+    assert lib.attn_fwd_plan(1, 1, 1, 1, 64, 7, ctypes.byref(n)) == E_UNSUPPORTED
+    assert lib.attn_fwd_plan(1, 1, 1, 1, 64, BF16, None) == E_NULLPTR
+    assert lib.attn_fwd_workspace_size(0, 1, 1, 1, 64, BF16) == 0
+    assert lib.attn_splitk_workspace_size(1, 1, 1, 64, 0) == 0
+    assert lib.attn_naive_scratch_size(1, 1, 1, 1, 9) == 0
+
+
+def test_python_binding_rejects_host_tensors(lib):
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sdpa.attn_fwd(q, q, q)
+    assert sdpa.attn_fwd_plan(8, 32, 1, 32768, 128, torch.bfloat16) == 8
+    with pytest.raises(sdpa.AttnError) as ei:
+        sdpa.attn_fwd_plan(1, 1, 1, 1, 96, torch.bfloat16)
+    assert ei.value.status == E_UNSUPPORTED
