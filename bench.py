@@ -15,7 +15,6 @@ the design notes; only the default line is the headline.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -41,20 +40,6 @@ def kv_bytes(w) -> float:
     return 2.0 * w.B * w.H * w.Sk * w.d * es
 
 
-def kernel_source_digest(path: str) -> str:
-    """Hash of the sources that define the timed kernels (for matching a
-    stored counter profile to the code it was taken on)."""
-    csrc = os.path.join(ROOT, "scaled_dot_product_flashattention_amd", "csrc")
-    files = {"fused": ["fwd_prefill.hip", "device_common.h"],
-             "splitk": ["fwd_splitk.hip", "device_common.h"],
-             "naive": ["naive.hip", "device_common.h"]}[path]
-    h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
-
-
 def stored_traffic(workload: str, path: str):
     """HBM bytes per launch from the committed counter profile of this
     workload, or None when there is none or the kernel source changed since."""
@@ -63,7 +48,9 @@ def stored_traffic(workload: str, path: str):
         return None
     with open(fn) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256") != kernel_source_digest(path):
+    from scaled_dot_product_flashattention_amd.profiling import source_digest
+
+    if rec.get("kernel_source_sha256") != source_digest(path):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -115,6 +102,9 @@ def main() -> int:
     ap.add_argument("--path", default="fused", choices=["fused", "naive", "splitk"])
     ap.add_argument("--n-split", type=int, default=None)
     ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, run 3 plain device copies of 256 MiB so a "
+                         "counter profile of this run can scale its byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -170,6 +160,14 @@ def main() -> int:
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_wall) * 1e3
     ms = e0.elapsed_time(e1) / args.steps
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     fl = flops(w)
     decode = args.path == "splitk" or n_split > 1

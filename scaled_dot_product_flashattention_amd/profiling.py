@@ -1,0 +1,146 @@
+"""Summaries of rocprofv3 results (rocpd SQLite databases) as short text.
+
+Used to keep the measured figures behind bench.py's roofline under profiles/:
+
+* kernel-trace summary: per kernel, dispatch count and mean / min / max
+  duration, from a ``rocprofv3 --kernel-trace --stats`` run;
+* HBM traffic: per-dispatch FETCH_SIZE and WRITE_SIZE (KiB) of one kernel from
+  two ``rocprofv3 --pmc`` runs, each scaled by what the same counter reads for a
+  plain device copy of known size in the same run (bench.py --copy-calibration
+  runs three 256 MiB copies).
+
+    python -m scaled_dot_product_flashattention_amd.profiling trace DB OUT.md --command "..."
+    python -m scaled_dot_product_flashattention_amd.profiling traffic FETCH_DB WRITE_DB \
+        --kernel fwd_prefill_kernel --workload medium_bf16 --path fused --command "..."
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sqlite3
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 256 << 20
+COPY_KERNEL = "copyBuffer"
+
+
+def kernel_trace(db_path: str):
+    db = sqlite3.connect(db_path)
+    rows = db.execute(
+        "select name, count(*), avg(duration), min(duration), max(duration), sum(duration) "
+        "from kernels group by name order by sum(duration) desc").fetchall()
+    return [dict(name=r[0], calls=r[1], avg_ns=r[2], min_ns=r[3], max_ns=r[4], total_ns=r[5])
+            for r in rows]
+
+
+def counter_per_kernel(db_path: str, counter: str):
+    db = sqlite3.connect(db_path)
+    rows = db.execute(
+        "select kernel_name, count(*), avg(value), avg(duration) from counters_collection "
+        "where counter_name = ? group by kernel_name", (counter,)).fetchall()
+    return {r[0]: dict(dispatches=r[1], kib=r[2], avg_ns=r[3]) for r in rows}
+
+
+def _pick(per_kernel: dict, needle: str):
+    hits = [(k, v) for k, v in per_kernel.items() if needle in k]
+    if len(hits) != 1:
+        raise SystemExit(f"expected one kernel matching {needle!r}, found {[k for k, _ in hits]}")
+    return hits[0]
+
+
+def source_digest(path: str) -> str:
+    csrc = os.path.join(ROOT, "scaled_dot_product_flashattention_amd", "csrc")
+    files = {"fused": ["fwd_prefill.hip", "device_common.h"],
+             "splitk": ["fwd_splitk.hip", "device_common.h"],
+             "naive": ["naive.hip", "device_common.h"]}[path]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def write_trace(db_path: str, out_md: str, command: str) -> None:
+    ks = kernel_trace(db_path)
+    lines = ["# Kernel trace summary", "", "Command:", "", "```", command, "```", "",
+             "| kernel | calls | mean us | min us | max us | total us |",
+             "|---|---|---|---|---|---|"]
+    for k in ks:
+        lines.append(f"| `{k['name'][:110]}` | {k['calls']} | {k['avg_ns'] / 1e3:.2f} | "
+                     f"{k['min_ns'] / 1e3:.2f} | {k['max_ns'] / 1e3:.2f} | {k['total_ns'] / 1e3:.1f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def write_traffic(fetch_db: str, write_db: str, kernel: str, workload: str, path: str,
+                  command: str) -> dict:
+    fetch = counter_per_kernel(fetch_db, "FETCH_SIZE")
+    write = counter_per_kernel(write_db, "WRITE_SIZE")
+    kname, kf = _pick(fetch, kernel)
+    _, kw = _pick(write, kernel)
+    _, cf = _pick(fetch, COPY_KERNEL)
+    _, cw = _pick(write, COPY_KERNEL)
+    f_scale = COPY_BYTES / (cf["kib"] * 1024.0)
+    w_scale = COPY_BYTES / (cw["kib"] * 1024.0)
+    fetch_b = kf["kib"] * 1024.0 * f_scale
+    write_b = kw["kib"] * 1024.0 * w_scale
+    rec = {
+        "workload": workload,
+        "path": path,
+        "kernel": kname,
+        "kernel_source_sha256": source_digest(path),
+        "fetch_kib_per_dispatch": kf["kib"],
+        "write_kib_per_dispatch": kw["kib"],
+        "copy_fetch_kib": cf["kib"],
+        "copy_write_kib": cw["kib"],
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "hbm_fetch_bytes_per_launch": fetch_b,
+        "hbm_write_bytes_per_launch": write_b,
+        "hbm_bytes_per_launch": fetch_b + write_b,
+        "command": command,
+    }
+    base = os.path.join(PROFILES, f"{workload}_{path}_traffic")
+    with open(base + ".json", "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = [f"# HBM traffic: {workload}, {path} path", "", "Commands (one counter per run):", "",
+             "```", command, "```", "",
+             f"Kernel: `{kname[:120]}`", "",
+             "| counter | KiB / dispatch | copy of 256 MiB reads | scale | bytes / launch |",
+             "|---|---|---|---|---|",
+             f"| FETCH_SIZE | {kf['kib']:.1f} | {cf['kib']:.1f} KiB | {f_scale:.4f} | {fetch_b:.4e} |",
+             f"| WRITE_SIZE | {kw['kib']:.1f} | {cw['kib']:.1f} KiB | {w_scale:.4f} | {write_b:.4e} |",
+             "", f"Total HBM bytes per launch: {fetch_b + write_b:.4e}",
+             f"Kernel source sha256 (fused kernel files): {rec['kernel_source_sha256']}"]
+    with open(base + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return rec
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("db")
+    t.add_argument("out")
+    t.add_argument("--command", required=True)
+    r = sub.add_parser("traffic")
+    r.add_argument("fetch_db")
+    r.add_argument("write_db")
+    r.add_argument("--kernel", required=True)
+    r.add_argument("--workload", required=True)
+    r.add_argument("--path", required=True)
+    r.add_argument("--command", required=True)
+    a = ap.parse_args()
+    if a.cmd == "trace":
+        write_trace(a.db, a.out, a.command)
+    else:
+        print(json.dumps(write_traffic(a.fetch_db, a.write_db, a.kernel, a.workload, a.path,
+                                       a.command), indent=1))
+
+
+if __name__ == "__main__":
+    main()
