@@ -79,6 +79,25 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
 // Base-2 exponential on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Sum of a packed pair of 16-bit values, accumulated in fp32 (v_dot2 with 1, 1).
+template <typename Tag> __device__ __forceinline__ float dot2_sum(uint32_t w, float acc);
+template <> __device__ __forceinline__ float dot2_sum<BF16>(uint32_t w, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+template <> __device__ __forceinline__ float dot2_sum<F16>(uint32_t w, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
+}
+
+// Value of the lane in the other half of the wave (lane ^ 32).
+__device__ __forceinline__ float swap_halves(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    // lanes 0-31 receive lanes 32-63 in r[1]; lanes 32-63 receive lanes 0-31 in r[0]
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 // Row (key) index held by result register r in lane half h: 8*(r/4) + 4*h + r%4.
 __device__ __forceinline__ constexpr int blk_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 

@@ -32,6 +32,10 @@ namespace attn {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
+// The running max moves only when a tile's max exceeds it by more than this
+// (base-2 units): probabilities then stay below 2^8 and most tiles skip the
+// rescale of the partial output.
+constexpr float kLazyRescale = 8.0f;
 
 struct PrefillParams {
     const void* q;
@@ -69,7 +73,7 @@ struct PrefillCfg {
     static_assert(BN * CPR % 256 == 0, "tile must split evenly over 256 threads");
 };
 
-template <typename Tag, int D, int NQ>
+template <typename Tag, int D, int NQ, bool PIPE>
 __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(PrefillParams p) {
     using C = PrefillCfg<Tag, D, NQ>;
     using T = typename Tag::storage;
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(PrefillParams p) {
     u32x4 kreg[C::KCH];
     u32x4 vreg[VCH][VREGS];
 
-    auto load_tile = [&](int t) {
+    auto load_k = [&](int t) {
         const int key0 = t * BN;
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -152,6 +156,10 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(PrefillParams p) {
             const int key = key0 + row;
             kreg[c] = key < nb ? *reinterpret_cast<const u32x4*>(kp + (int64_t)key * p.sk.s + cc * C::EPC) : z;
         }
+    };
+    auto load_v = [&](int t) {
+        const int key0 = t * BN;
+        const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int c = 0; c < VCH; ++c) {
             const int idx = tid + c * 256;
@@ -160,30 +168,6 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(PrefillParams p) {
             for (int e = 0; e < VREGS; ++e) {
                 const int key = key0 + pr * VREGS + e;
                 vreg[c][e] = key < nb ? *reinterpret_cast<const u32x4*>(vp + (int64_t)key * p.sk.s + cc * C::EPC) : z;
-            }
-        }
-    };
-
-    auto store_tile = [&](int buf) {
-        T* Ks = reinterpret_cast<T*>(smem + buf * C::STAGE_BYTES);
-        T* Vt = Ks + C::K_ELEMS;
-#pragma unroll
-        for (int c = 0; c < C::KCH; ++c) {
-            const int idx = tid + c * 256;
-            const int row = idx / C::CPR, cc = idx - row * C::CPR;
-            *reinterpret_cast<u32x4*>(Ks + row * C::KROW + cc * C::EPC) = kreg[c];
-        }
-#pragma unroll
-        for (int c = 0; c < VCH; ++c) {
-            const int idx = tid + c * 256;
-            const int pr = idx / C::CPR, cc = idx - pr * C::CPR;
-            if constexpr (k16) {
-                // vreg[c][0] = V[2pr][8cc .. +7], vreg[c][1] = V[2pr+1][8cc .. +7]
-                store_pair_transposed(Vt, C::VROW, cc, pr, vreg[c][0], vreg[c][1]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    reinterpret_cast<uint32_t*>(Vt)[(cc * 4 + e) * C::VROW + pr] = vreg[c][0][e];
             }
         }
     };
@@ -202,129 +186,221 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(PrefillParams p) {
     }
     const float c = p.c;
 
-    if (ntiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
+    auto k_lds = [&](int tile) {
+        return reinterpret_cast<const T*>(smem + (tile & 1) * C::STAGE_BYTES);
+    };
+    auto v_lds = [&](int tile) { return k_lds(tile) + C::K_ELEMS; };
+    auto active = [&](int tile) { return wave_active && tile * BN < wave_kend; };
 
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < ntiles) load_tile(t + 1);
+    // -- S^T = K Q^T for one key tile (keys x queries, BN/32 blocks of 32) -----
+    auto qk_tile = [&](const T* Ks, f32x16 (&sacc)[BN / 32][NQ]) {
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+            for (int gq = 0; gq < NQ; ++gq)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[kb][gq][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < QSTEPS; ++s) {
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb) {
+                const T* krow = Ks + (kb * 32 + n32) * C::KROW;
+                if constexpr (k16) {
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(krow + s * 16 + hh * 8);
+#pragma unroll
+                    for (int gq = 0; gq < NQ; ++gq) sacc[kb][gq] = mfma16<Tag>(a, qop[gq][s], sacc[kb][gq]);
+                } else {
+                    const float a = krow[2 * s + hh];
+#pragma unroll
+                    for (int gq = 0; gq < NQ; ++gq) sacc[kb][gq] = mfma_f32(a, qop[gq][s], sacc[kb][gq]);
+                }
+            }
+        }
+    };
 
-        if (wave_active && t * BN < wave_kend) {
-            const T* Ks = reinterpret_cast<const T*>(smem + buf * C::STAGE_BYTES);
-            const T* Vt = Ks + C::K_ELEMS;
-
-            // -- scores S^T (keys x queries), 2 key blocks of 32 -------------
-            f32x16 sacc[BN / 32][NQ];
+    // -- online softmax of one tile: running max (moved lazily), probabilities
+    //    rounded to the input type and packed in pairs, running sum -----------
+    // pk[gq][kb][w] holds the probabilities of result registers 2w and 2w+1.
+    constexpr int PKW = k16 ? 8 : 1;
+    uint32_t pk[NQ][BN / 32][PKW];
+    auto softmax_tile = [&](auto masked_tag, f32x16 (&sacc)[BN / 32][NQ], int tile) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+#pragma unroll
+        for (int gq = 0; gq < NQ; ++gq) {
+            if constexpr (MASKED) {
+                const int qi = qw0 + gq * 32 + n32;
+                const int lim = p.causal ? min(nb, qi + 1) : nb;
+#pragma unroll
+                for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (tile * BN + kb * 32 + blk_row(r, hh) >= lim) sacc[kb][gq][r] = kNegInf;
+            }
+            // row max: four independent max3 chains, then the other lane half
+            float mq[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
             for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-                for (int gq = 0; gq < NQ; ++gq)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sacc[kb][gq][r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < QSTEPS; ++s) {
-#pragma unroll
-                for (int kb = 0; kb < BN / 32; ++kb) {
-                    const T* krow = Ks + (kb * 32 + n32) * C::KROW;
-                    if constexpr (k16) {
-                        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + s * 16 + hh * 8);
-#pragma unroll
-                        for (int gq = 0; gq < NQ; ++gq) sacc[kb][gq] = mfma16<Tag>(a, qop[gq][s], sacc[kb][gq]);
-                    } else {
-                        const float a = krow[2 * s + hh];
-#pragma unroll
-                        for (int gq = 0; gq < NQ; ++gq) sacc[kb][gq] = mfma_f32(a, qop[gq][s], sacc[kb][gq]);
-                    }
+                for (int r = 0; r < 16; r += 8) {
+                    const int ch = (kb * 2 + r / 8) & 3;
+                    mq[ch] = fmaxf(mq[ch], fmaxf(sacc[kb][gq][r], sacc[kb][gq][r + 1]));
+                    mq[ch] = fmaxf(mq[ch], fmaxf(sacc[kb][gq][r + 2], sacc[kb][gq][r + 3]));
+                    mq[ch] = fmaxf(mq[ch], fmaxf(sacc[kb][gq][r + 4], sacc[kb][gq][r + 5]));
+                    mq[ch] = fmaxf(mq[ch], fmaxf(sacc[kb][gq][r + 6], sacc[kb][gq][r + 7]));
                 }
-            }
-
-            // -- online softmax update, one query per lane and group ---------
-            const bool need_mask = (t + 1) * BN > wave_lim_min;
-#pragma unroll
-            for (int gq = 0; gq < NQ; ++gq) {
-                const int qi = qw0 + gq * 32 + n32;
-                const int lim = p.causal ? min(nb, qi + 1) : nb;
-                float mx = kNegInf;
-                if (need_mask) {
-#pragma unroll
-                    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int j = t * BN + kb * 32 + blk_row(r, hh);
-                            if (j >= lim) sacc[kb][gq][r] = kNegInf;
-                        }
-                }
-#pragma unroll
-                for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][gq][r]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float mxs = (mx == kNegInf) ? kNegInf : mx * c;
+            float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+            mx = fmaxf(mx, swap_halves(mx));
+            const float mxs = (MASKED && mx == kNegInf) ? kNegInf : mx * c;
+            // move the reference max only when the tile max exceeds it by more
+            // than kLazyRescale (log2 units); the wave decides together.
+            if (__any(mxs > m_run[gq] + kLazyRescale)) {
                 const float m_new = fmaxf(m_run[gq], mxs);
-                const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-                const float alpha = fast_exp2(m_run[gq] - m_use);
+                const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run[gq] - m_new);
                 m_run[gq] = m_new;
-                float rs = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float x = sacc[kb][gq][r];
-                        float pr = fast_exp2(fmaf(x, c, -m_use));
-                        if (need_mask) pr = (x == kNegInf) ? 0.f : pr;
-                        sacc[kb][gq][r] = pr;
-                        rs += pr;
-                    }
-                l_run[gq] = l_run[gq] * alpha + rs;
+                l_run[gq] *= alpha;
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) oacc[gq][db][r] *= alpha;
             }
+            const float m_use = (m_run[gq] == kNegInf) ? 0.f : m_run[gq];
+            float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const float x0 = sacc[kb][gq][r], x1 = sacc[kb][gq][r + 1];
+                    float p0 = fast_exp2(fmaf(x0, c, -m_use));
+                    float p1 = fast_exp2(fmaf(x1, c, -m_use));
+                    if constexpr (MASKED) {
+                        p0 = (x0 == kNegInf) ? 0.f : p0;
+                        p1 = (x1 == kNegInf) ? 0.f : p1;
+                    }
+                    if constexpr (k16) {
+                        const uint32_t w2 = pack2<Tag>(p0, p1);
+                        pk[gq][kb][r / 2] = w2;
+                        rs[(r / 2) & 3] = dot2_sum<Tag>(w2, rs[(r / 2) & 3]);
+                    } else {
+                        sacc[kb][gq][r] = p0;
+                        sacc[kb][gq][r + 1] = p1;
+                        rs[(r / 2) & 3] += p0 + p1;
+                    }
+                }
+            l_run[gq] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+        }
+    };
 
-            // -- O^T += V^T P^T ------------------------------------------------
+    // -- O^T += V^T P^T ----------------------------------------------------------
+    auto pv_tile = [&](const T* Vt, f32x16 (&sacc)[BN / 32][NQ]) {
 #pragma unroll
-            for (int kb = 0; kb < BN / 32; ++kb) {
-                if constexpr (k16) {
+        for (int kb = 0; kb < BN / 32; ++kb) {
+            if constexpr (k16) {
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        u32x4 pop[NQ];
+                for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) {
+                        const T* vrow = Vt + (db * 32 + n32) * C::VROW + kb * 32 + 16 * u + 4 * hh;
+                        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+                        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+                        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
                         for (int gq = 0; gq < NQ; ++gq) {
-                            const f32x16& sv = sacc[kb][gq];
-                            pop[gq] = u32x4{pack2<Tag>(sv[8 * u + 0], sv[8 * u + 1]),
-                                            pack2<Tag>(sv[8 * u + 2], sv[8 * u + 3]),
-                                            pack2<Tag>(sv[8 * u + 4], sv[8 * u + 5]),
-                                            pack2<Tag>(sv[8 * u + 6], sv[8 * u + 7])};
-                        }
-#pragma unroll
-                        for (int db = 0; db < D / 32; ++db) {
-                            const T* vrow = Vt + (db * 32 + n32) * C::VROW + kb * 32 + 16 * u + 4 * hh;
-                            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-                            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-                            const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-                            for (int gq = 0; gq < NQ; ++gq) oacc[gq][db] = mfma16<Tag>(a, pop[gq], oacc[gq][db]);
+                            const u32x4 b = {pk[gq][kb][4 * u], pk[gq][kb][4 * u + 1], pk[gq][kb][4 * u + 2],
+                                             pk[gq][kb][4 * u + 3]};
+                            oacc[gq][db] = mfma16<Tag>(a, b, oacc[gq][db]);
                         }
                     }
-                } else {
+                }
+            } else {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
+                for (int r = 0; r < 16; ++r) {
 #pragma unroll
-                        for (int db = 0; db < D / 32; ++db) {
-                            const float a = Vt[(db * 32 + n32) * C::VROW + kb * 32 + blk_row(r, hh)];
+                    for (int db = 0; db < D / 32; ++db) {
+                        const float a = Vt[(db * 32 + n32) * C::VROW + kb * 32 + blk_row(r, hh)];
 #pragma unroll
-                            for (int gq = 0; gq < NQ; ++gq) oacc[gq][db] = mfma_f32(a, sacc[kb][gq][r], oacc[gq][db]);
-                        }
+                        for (int gq = 0; gq < NQ; ++gq) oacc[gq][db] = mfma_f32(a, sacc[kb][gq][r], oacc[gq][db]);
                     }
                 }
             }
         }
+    };
 
-        if (t + 1 < ntiles) store_tile(buf ^ 1);
+    // ---- key loop ----------------------------------------------------------------
+    // PIPE: LDS holds K of tile t+1 and V of tile t while tile t is processed,
+    // so the scores of tile t+1 are issued before the softmax of tile t (K is
+    // staged two tiles ahead, V one). Without PIPE both are staged one ahead
+    // and tile t's scores are computed at the start of its iteration. K_t and
+    // V_t live in LDS stage t & 1.
+    constexpr int KAHEAD = PIPE ? 2 : 1;
+    auto store_k = [&](int tile) {
+        T* Ks = reinterpret_cast<T*>(smem + (tile & 1) * C::STAGE_BYTES);
+#pragma unroll
+        for (int cc2 = 0; cc2 < C::KCH; ++cc2) {
+            const int idx = tid + cc2 * 256;
+            const int row = idx / C::CPR, cc = idx - row * C::CPR;
+            *reinterpret_cast<u32x4*>(Ks + row * C::KROW + cc * C::EPC) = kreg[cc2];
+        }
+    };
+    auto store_v = [&](int tile) {
+        T* Vt = reinterpret_cast<T*>(smem + (tile & 1) * C::STAGE_BYTES) + C::K_ELEMS;
+#pragma unroll
+        for (int c2 = 0; c2 < VCH; ++c2) {
+            const int idx = tid + c2 * 256;
+            const int pr = idx / C::CPR, cc = idx - pr * C::CPR;
+            if constexpr (k16) {
+                store_pair_transposed(Vt, C::VROW, cc, pr, vreg[c2][0], vreg[c2][1]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    reinterpret_cast<uint32_t*>(Vt)[(cc * 4 + e) * C::VROW + pr] = vreg[c2][0][e];
+            }
+        }
+    };
+
+    f32x16 s_cur[BN / 32][NQ];
+    if (ntiles > 0) {
+        load_v(0);
+        store_v(0);
+#pragma unroll
+        for (int a = 0; a < KAHEAD; ++a)
+            if (a < ntiles) {
+                load_k(a);
+                store_k(a);
+            }
+    }
+    __syncthreads();
+    if constexpr (PIPE) {
+        if (ntiles > 0 && active(0)) qk_tile(k_lds(0), s_cur);
+        __syncthreads();  // every wave has read K_0 before its stage is reused
+    }
+
+    for (int t = 0; t < ntiles; ++t) {
+        if (t + KAHEAD < ntiles) load_k(t + KAHEAD);
+        if (t + 1 < ntiles) load_v(t + 1);
+
+        f32x16 s_next[BN / 32][NQ];
+        if constexpr (PIPE) {
+            if (t + 1 < ntiles && active(t + 1)) qk_tile(k_lds(t + 1), s_next);
+        } else {
+            if (active(t)) qk_tile(k_lds(t), s_cur);
+        }
+
+        if (active(t)) {
+            if ((t + 1) * BN > wave_lim_min)
+                softmax_tile(std::true_type{}, s_cur, t);
+            else
+                softmax_tile(std::false_type{}, s_cur, t);
+            pv_tile(v_lds(t), s_cur);
+        }
+        if constexpr (PIPE) {
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                for (int gq = 0; gq < NQ; ++gq) s_cur[kb][gq] = s_next[kb][gq];
+        }
+
+        if (t + KAHEAD < ntiles) store_k(t + KAHEAD);
+        if (t + 1 < ntiles) store_v(t + 1);
         __syncthreads();
     }
 
@@ -366,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(PrefillParams p) {
     }
 }
 
-template <typename Tag, int D, int NQ>
+template <typename Tag, int D, int NQ, bool PIPE>
 hipError_t launch_prefill(const FwdArgs& a, hipStream_t stream) {
     using C = PrefillCfg<Tag, D, NQ>;
     PrefillParams p;
@@ -388,21 +464,15 @@ hipError_t launch_prefill(const FwdArgs& a, hipStream_t stream) {
     const int64_t grid = (int64_t)p.n_qtiles * a.B * a.H;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     p.remap = (grid % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((fwd_prefill_kernel<Tag, D, NQ>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((fwd_prefill_kernel<Tag, D, NQ, PIPE>), dim3((unsigned)grid), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t run_prefill(const FwdArgs& a, hipStream_t stream) {
-    switch (a.dtype) {
-    case 2:
-        return a.d == 64 ? launch_prefill<BF16, 64, 1>(a, stream) : launch_prefill<BF16, 128, 1>(a, stream);
-    case 1:
-        return a.d == 64 ? launch_prefill<F16, 64, 1>(a, stream) : launch_prefill<F16, 128, 1>(a, stream);
-    default:
-        return a.d == 64 ? launch_prefill<F32, 64, 1>(a, stream) : launch_prefill<F32, 128, 1>(a, stream);
-    }
+    if (a.dtype != 0) return run_prefill16(a, stream);
+    return a.d == 64 ? launch_prefill<F32, 64, 1, false>(a, stream) : launch_prefill<F32, 128, 1, false>(a, stream);
 }
 
 }  // namespace attn

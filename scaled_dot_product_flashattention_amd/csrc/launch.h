@@ -22,8 +22,9 @@ struct FwdArgs {
     int dtype;   // 0 = fp32, 1 = fp16, 2 = bf16
 };
 
-// Fused single-kernel forward (any shape).
+// Fused single-kernel forward (any shape); 16-bit inputs go to run_prefill16.
 hipError_t run_prefill(const FwdArgs& a, hipStream_t stream);
+hipError_t run_prefill16(const FwdArgs& a, hipStream_t stream);
 
 // Split-over-keys forward: partial kernel + merge kernel.
 size_t splitk_workspace_bytes(int B, int H, int Sq, int d, int n_split);

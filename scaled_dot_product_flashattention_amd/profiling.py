@@ -53,7 +53,7 @@ def _pick(per_kernel: dict, needle: str):
 
 def source_digest(path: str) -> str:
     csrc = os.path.join(ROOT, "scaled_dot_product_flashattention_amd", "csrc")
-    files = {"fused": ["fwd_prefill.hip", "device_common.h"],
+    files = {"fused": ["fwd_prefill.hip", "fwd_prefill16.hip", "device_common.h"],
              "splitk": ["fwd_splitk.hip", "device_common.h"],
              "naive": ["naive.hip", "device_common.h"]}[path]
     h = hashlib.sha256()
