@@ -89,3 +89,14 @@ def test_determinism():
 @pytest.mark.parametrize("name", ["medium_bf16", "long_causal_bf16", "bert_pad_fp16", "decode_bf16"])
 def test_workload_full_size_sampled(name):
     sampled_case(W[name])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("layout,causal,pad", [("bhsd", False, False), ("bshd", True, False),
+                                               ("bhsd", True, True), ("bshd", False, True)])
+def test_long_keys_head64(dtype, layout, causal, pad):
+    """Head size 64 over >= 2048 keys (the 8-wave kernel), ragged lengths."""
+    w = W["medium_bf16"].replace(name="long64", B=2 if pad else 1, H=2, Sq=2100, Sk=2300,
+                                 dtype=dtype, layout=layout, causal=causal,
+                                 kv_len_range=(1500, 2300) if pad else None, seed=31)
+    full_case(w, poison=pad)
