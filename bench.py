@@ -40,9 +40,10 @@ def kv_bytes(w) -> float:
     return 2.0 * w.B * w.H * w.Sk * w.d * es
 
 
-def stored_traffic(workload: str, path: str):
-    """HBM bytes per launch from the committed counter profile of this
-    workload, or None when there is none or the kernel source changed since."""
+def stored_traffic(workload: str, path: str, kind: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    profile of this workload, or None when there is none or the kernel's
+    source (family ``kind``: fused, splitk, naive) changed since."""
     fn = os.path.join(PROFILES, f"{workload}_{path}_traffic.json")
     if not os.path.exists(fn):
         return None
@@ -50,7 +51,7 @@ def stored_traffic(workload: str, path: str):
         rec = json.load(f)
     from scaled_dot_product_flashattention_amd.profiling import source_digest
 
-    if rec.get("kernel_source_sha256") != source_digest(path):
+    if rec.get("kernel_source_sha256") != source_digest(kind):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -161,6 +162,7 @@ def main() -> int:
     wall_ms = (time.perf_counter() - t_wall) * 1e3
     ms = e0.elapsed_time(e1) / args.steps
 
+    peak_bytes = torch.cuda.max_memory_allocated(dev)
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -186,7 +188,8 @@ def main() -> int:
         else:
             metric = f"attention fwd TFLOP/s ({args.path}), {w.description}"
         value, unit = tflops, "TFLOP/s"
-    roof["traffic"] = stored_traffic(args.config, args.path)
+    kind = "splitk" if decode else args.path
+    roof["traffic"] = stored_traffic(args.config, args.path, kind)
     roof["kernel_ms"] = round(ms, 5)
     roof["algorithmic_units"] = ("bytes of K and V per launch" if decode else "FLOPs per launch")
     roof["algorithmic_per_launch"] = kv_bytes(w) if decode else fl
@@ -206,7 +209,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "B": B, "H": H, "Sq": Sq,
                    "Sk": Sk, "d": d, "layout": w.layout, "causal": w.causal, "path": args.path,
-                   "n_split": n_split, "flops_per_step": fl, "wall_ms_timed_region": round(wall_ms, 2)},
+                   "n_split": n_split, "flops_per_step": fl, "wall_ms_timed_region": round(wall_ms, 2),
+                   "peak_device_bytes": peak_bytes},
         "roofline": roof,
     }
     if not args.skip_cpu_baseline:

@@ -10,7 +10,9 @@
 // by exp(m_old - m_new) first. The output is divided by l once, at the end.
 //
 // Mapping to gfx950:
-//   * 4 waves per workgroup, each owning 32*NQ query rows.
+//   * 4 waves per workgroup, each owning 32*NQ query rows (KSPLIT = 1), or 8
+//     waves in two groups that each take half of every key tile (KSPLIT = 2,
+//     see the ping-pong loop below).
 //   * Scores are computed transposed, S^T = K Q^T, on 32x32x16 matrix-core
 //     blocks: a lane owns one query (its column) and half the keys of each
 //     32-key block (its rows), so row max and row sum are in-lane but for one
@@ -25,9 +27,11 @@
 //     the K operand reads (ds_read_b128) and the transposing V operand reads
 //     (ds_read_b64_tr_b16) are free of bank conflicts.
 //   * PIPE: the scores of tile t+1 are issued before the softmax of tile t.
-//   * The running max moves lazily (only when a tile beats it by more than
-//     2^8), so most tiles skip the rescale of the partial output; the result
-//     is the same up to rounding because m, l and O always share one m.
+//   * The running max serves as a reference: a tile's probabilities are taken
+//     against it directly, and the exact tile max (with the rescale of l and
+//     O) is computed only on a row's first tile or when the tile's row sum
+//     shows the reference fell far behind. The result is the same up to
+//     rounding because m, l and O always share one m.
 //   * Workgroups of one head stay on one XCD (its L2 then serves every re-read
 //     of that head's K/V); causal tiles start longest-first.
 #include "device_common.h"
@@ -38,9 +42,6 @@ namespace attn {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
-// The running max moves only when a tile's max exceeds it by more than this
-// (base-2 units): probabilities then stay below 2^8.
-constexpr float kLazyRescale = 8.0f;
 // A tile whose probabilities against the reference max sum to more than this
 // (per lane, or are not finite) takes the exact-max path.
 constexpr float kRefGuard = 4294967296.0f;  // 2^32

@@ -9,7 +9,8 @@ Used to keep the measured figures behind bench.py's roofline under profiles/:
   plain device copy of known size in the same run (bench.py --copy-calibration
   runs three 256 MiB copies).
 
-    python -m scaled_dot_product_flashattention_amd.profiling trace DB OUT.md --command "..."
+    python -m scaled_dot_product_flashattention_amd.profiling trace DB OUT.md --command "..." \
+        [--timed STEPS --bench-log LOG]
     python -m scaled_dot_product_flashattention_amd.profiling traffic FETCH_DB WRITE_DB \
         --kernel fwd_prefill_kernel --workload medium_bf16 --path fused --command "..."
 """
@@ -19,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sqlite3
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -51,26 +53,67 @@ def _pick(per_kernel: dict, needle: str):
     return hits[0]
 
 
-def source_digest(path: str) -> str:
+def kernel_kind(kernel_name: str) -> str:
+    """Which source family a kernel comes from: fused, splitk or naive."""
+    if "splitk" in kernel_name:
+        return "splitk"
+    if "naive" in kernel_name:
+        return "naive"
+    return "fused"
+
+
+def source_digest(kind: str) -> str:
+    """sha256 over the sources of one kernel family (fused, splitk, naive)."""
     csrc = os.path.join(ROOT, "scaled_dot_product_flashattention_amd", "csrc")
     files = {"fused": ["fwd_prefill.hip", "fwd_prefill16.hip", "device_common.h"],
              "splitk": ["fwd_splitk.hip", "device_common.h"],
-             "naive": ["naive.hip", "device_common.h"]}[path]
+             "naive": ["naive.hip", "device_common.h"]}[kind]
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f)) as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()
 
 
-def write_trace(db_path: str, out_md: str, command: str) -> None:
+def code_only(src: str) -> str:
+    """C/C++ source without comments and blank lines, so that an edit of a
+    comment does not count as a change of the kernel."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+
+
+def timed_means(db_path: str, last: int):
+    """Per kernel, the mean duration (ns) of its last ``last`` dispatches in
+    start order: the dispatches of bench.py's timed region."""
+    db = sqlite3.connect(db_path)
+    by: dict[str, list[int]] = {}
+    for name, start, end in db.execute("select name, start, end from kernels order by start"):
+        by.setdefault(name, []).append(end - start)
+    return {n: sum(d[-last:]) / last for n, d in by.items() if len(d) >= last}
+
+
+def write_trace(db_path: str, out_md: str, command: str, timed: int = 0,
+                bench_line: str | None = None) -> None:
     ks = kernel_trace(db_path)
+    tm = timed_means(db_path, timed) if timed else {}
     lines = ["# Kernel trace summary", "", "Command:", "", "```", command, "```", "",
-             "| kernel | calls | mean us | min us | max us | total us |",
-             "|---|---|---|---|---|---|"]
+             "| kernel | calls | mean us | min us | max us | total us |"
+             + (f" mean of last {timed} us |" if timed else ""),
+             "|---|---|---|---|---|---|" + ("---|" if timed else "")]
     for k in ks:
-        lines.append(f"| `{k['name'][:110]}` | {k['calls']} | {k['avg_ns'] / 1e3:.2f} | "
-                     f"{k['min_ns'] / 1e3:.2f} | {k['max_ns'] / 1e3:.2f} | {k['total_ns'] / 1e3:.1f} |")
+        row = (f"| `{k['name'][:110]}` | {k['calls']} | {k['avg_ns'] / 1e3:.2f} | "
+               f"{k['min_ns'] / 1e3:.2f} | {k['max_ns'] / 1e3:.2f} | {k['total_ns'] / 1e3:.1f} |")
+        if timed:
+            row += f" {tm[k['name']] / 1e3:.2f} |" if k["name"] in tm else " - |"
+        lines.append(row)
+    if timed:
+        lines += ["", f"The last {timed} dispatches of a kernel are the ones bench.py times "
+                  "(its warmup dispatches come first)."]
+    if bench_line:
+        rec = json.loads(bench_line)
+        lines += ["", f"bench.py in the same run: {rec['value']} {rec['unit']}, "
+                  f"{rec['ms_per_step'] * 1e3:.2f} us per step (HIP events over the timed region)."]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -91,7 +134,7 @@ def write_traffic(fetch_db: str, write_db: str, kernel: str, workload: str, path
         "workload": workload,
         "path": path,
         "kernel": kname,
-        "kernel_source_sha256": source_digest(path),
+        "kernel_source_sha256": source_digest(kernel_kind(kname)),
         "fetch_kib_per_dispatch": kf["kib"],
         "write_kib_per_dispatch": kw["kib"],
         "copy_fetch_kib": cf["kib"],
@@ -114,7 +157,7 @@ def write_traffic(fetch_db: str, write_db: str, kernel: str, workload: str, path
              f"| FETCH_SIZE | {kf['kib']:.1f} | {cf['kib']:.1f} KiB | {f_scale:.4f} | {fetch_b:.4e} |",
              f"| WRITE_SIZE | {kw['kib']:.1f} | {cw['kib']:.1f} KiB | {w_scale:.4f} | {write_b:.4e} |",
              "", f"Total HBM bytes per launch: {fetch_b + write_b:.4e}",
-             f"Kernel source sha256 (fused kernel files): {rec['kernel_source_sha256']}"]
+             f"Kernel source sha256 ({kernel_kind(kname)} kernel files): {rec['kernel_source_sha256']}"]
     with open(base + ".md", "w") as f:
         f.write("\n".join(lines) + "\n")
     return rec
@@ -127,6 +170,10 @@ def main() -> None:
     t.add_argument("db")
     t.add_argument("out")
     t.add_argument("--command", required=True)
+    t.add_argument("--timed", type=int, default=0,
+                   help="also average each kernel's last N dispatches (bench.py --steps N)")
+    t.add_argument("--bench-log", default=None,
+                   help="file holding bench.py's JSON line from the same run")
     r = sub.add_parser("traffic")
     r.add_argument("fetch_db")
     r.add_argument("write_db")
@@ -136,7 +183,11 @@ def main() -> None:
     r.add_argument("--command", required=True)
     a = ap.parse_args()
     if a.cmd == "trace":
-        write_trace(a.db, a.out, a.command)
+        line = None
+        if a.bench_log:
+            with open(a.bench_log) as f:
+                line = [x for x in f.read().splitlines() if x.startswith("{")][-1]
+        write_trace(a.db, a.out, a.command, a.timed, line)
     else:
         print(json.dumps(write_traffic(a.fetch_db, a.write_db, a.kernel, a.workload, a.path,
                                        a.command), indent=1))
