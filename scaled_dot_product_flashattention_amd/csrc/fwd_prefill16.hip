@@ -10,28 +10,33 @@
 // by exp(m_old - m_new) first. The output is divided by l once, at the end.
 //
 // Mapping to gfx950:
-//   * 4 waves per workgroup, each owning 32*NQ query rows (KSPLIT = 1), or 8
-//     waves in two groups that each take half of every key tile (KSPLIT = 2,
-//     see the ping-pong loop below).
 //   * Scores are computed transposed, S^T = K Q^T, on 32x32x16 matrix-core
 //     blocks: a lane owns one query (its column) and half the keys of each
 //     32-key block (its rows), so row max and row sum are in-lane but for one
 //     exchange between the two lane halves (v_permlane32_swap).
 //   * The output is kept transposed too, O^T += V^T P^T: probabilities feed
 //     the second product straight from the score registers (rounded and
-//     packed in pairs), and the rescale touches only the lane's own query.
+//     packed in pairs), and a rescale touches only the lane's own query.
+//   * Software pipeline inside each wave: while the vector unit computes the
+//     softmax of key tile t, the same wave issues the matrix products of
+//     P(t-1) V(t-1) and K(t+1) Q^T, one product between every few
+//     probabilities. On gfx950 a wave's own vector instructions issue while
+//     its matrix product runs; those of another wave on the same SIMD wait
+//     for the matrix unit, so the overlap has to come from within the wave.
 //   * K and V tiles travel global -> LDS by direct DMA loads
-//     (global_load_lds_dwordx4) into an NST-stage ring, NST-1 tiles ahead of
-//     the one being computed; no registers are spent on staging. Both sit in
-//     LDS row-major with their 16-byte chunks XOR-swizzled per row so that
-//     the K operand reads (ds_read_b128) and the transposing V operand reads
-//     (ds_read_b64_tr_b16) are free of bank conflicts.
-//   * PIPE: the scores of tile t+1 are issued before the softmax of tile t.
-//   * The running max serves as a reference: a tile's probabilities are taken
-//     against it directly, and the exact tile max (with the rescale of l and
-//     O) is computed only on a row's first tile or when the tile's row sum
-//     shows the reference fell far behind. The result is the same up to
-//     rounding because m, l and O always share one m.
+//     (global_load_lds_dwordx4) into an NST-stage ring, NST-2 tiles ahead of
+//     the tile whose keys are multiplied; no registers are spent on staging.
+//     Both sit in LDS row-major with their 16-byte chunks XOR-swizzled per
+//     row so that the K operand reads (ds_read_b128) and the transposing V
+//     operand reads (ds_read_b64_tr_b16) are free of bank conflicts.
+//   * KSPLIT = 2: two groups of 4 waves take the two key halves of every
+//     tile for the same queries (each key operand then feeds two query
+//     blocks), and merge their (m, l, O) through LDS at the end.
+//   * The running max is a reference: probabilities are taken against it
+//     directly and only the row sum is checked. The exact max (with the
+//     rescale of l and O) is computed only when a sum leaves
+//     [2^-100, 2^32], which for typical scores happens on a row's first tiles
+//     at most. Any common reference gives the same softmax.
 //   * Workgroups of one head stay on one XCD (its L2 then serves every re-read
 //     of that head's K/V); causal tiles start longest-first.
 #include "device_common.h"
@@ -42,13 +47,17 @@ namespace attn {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
-// A tile whose probabilities against the reference max sum to more than this
-// (per lane, or are not finite) takes the exact-max path.
-constexpr float kRefGuard = 4294967296.0f;  // 2^32
+// The reference max stays while every lane's running sum lies in
+// [2^-100, 2^32] (bit patterns below): probabilities then neither overflow
+// nor lose precision to underflow.
+constexpr uint32_t kSumLoBits = 0x0D800000u;  // 2^-100
+constexpr uint32_t kSumHiBits = 0x4F800000u;  // 2^32
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <int V> using int_c = std::integral_constant<int, V>;
 
 struct Prefill16Params {
     const void* q;
@@ -98,17 +107,21 @@ __device__ __forceinline__ void barrier_nofence() {
     asm volatile("" ::: "memory");
 }
 
-// KSPLIT = 1: 4 waves, wave w owns queries [32*NQ*w, +32*NQ) of the tile
-//   and every key of every key tile.
-// KSPLIT = 2: 8 waves; wave w owns queries [32*NQ*(w%4), +32*NQ) and the key
-//   half (w/4) of every key tile, so each key/value operand read from LDS
-//   feeds twice as many products per query row; the two halves' (m, l, O)
-//   are merged through LDS after the key loop.
-template <typename Tag, int D, int NQ, int BN, int NST, bool PIPE, int KSPLIT>
+// True where a running sum left [2^-100, 2^32] (or is not a number).
+__device__ __forceinline__ bool sum_out_of_range(float l) {
+    return (__float_as_uint(l) - kSumLoBits) > (kSumHiBits - kSumLoBits);
+}
+
+// Template parameters:
+//   D      head size (64 or 128)
+//   NQ     32-query blocks per wave (BM = 128 * NQ queries per workgroup)
+//   BN     keys per tile
+//   NST    LDS ring stages (NST - 2 tiles in flight ahead)
+//   KSPLIT 1: 4 waves, each over all keys of a tile; 2: 8 waves, wave w
+//          takes key half w / 4 of every tile for the queries of wave w % 4
+template <typename Tag, int D, int NQ, int BN, int NST, int KSPLIT>
 __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel(Prefill16Params p) {
     constexpr int NT = 256 * KSPLIT;               // threads
-    constexpr int NW = 4 * KSPLIT;                 // waves
-    constexpr int BM = 4 * 32 * NQ;                // query rows per workgroup
     constexpr int KBW = BN / 32 / KSPLIT;          // 32-key blocks per wave and tile
     constexpr int RB = D * 2;                      // bytes per K/V row
     constexpr int CPR = RB / 16;                   // 16-byte chunks per row
@@ -116,19 +129,24 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
     constexpr int STAGE_B = 2 * TILE_B;            // K tile, then V tile
     constexpr int DMA1 = TILE_B / 16 / NT;         // DMA loads per thread, tensor and tile
     constexpr int DPT = 2 * DMA1;                  // ... for K and V
-    constexpr int P = NST - 1;                     // tiles in flight ahead
+    constexpr int P = NST - 2;                     // tiles issued ahead
     constexpr int OROW = D + 8;                    // output staging row (elements)
     constexpr int OUT_B = 4 * 32 * NQ * OROW * 2;
     constexpr int MRG_W = (NQ * (D / 32) * 16 + 2 * NQ) * 64 * 4;  // one wave's (O, m, l) in fp32
     constexpr int MRG_B = KSPLIT == 2 ? 4 * MRG_W : 0;
     constexpr int LDS_A = NST * STAGE_B > OUT_B ? NST * STAGE_B : OUT_B;
     constexpr int LDS_B = LDS_A > MRG_B ? LDS_A : MRG_B;
+    constexpr int NPV = KBW * 2 * (D / 32) * NQ;   // products of P V per tile and wave
+    constexpr int NQK = (D / 16) * KBW * NQ;       // products of K Q^T per tile and wave
+    constexpr int NM = NPV + NQK;
+    constexpr int NPAIR = NQ * KBW * 8;            // probability pairs per lane and tile
     static_assert(KBW >= 1 && BN % (32 * KSPLIT) == 0, "key tile must split over the wave groups");
     static_assert(DMA1 >= 1 && TILE_B % (16 * NT) == 0, "tile must split over the lanes");
-    static_assert(P >= (PIPE ? 2 : 1), "pipelining needs a deeper ring");
-    static_assert(P * DPT < 64, "vmcnt range");
+    static_assert(P >= 2, "the pipeline needs two tiles in flight");
+    static_assert((P - 2) * DPT < 64, "vmcnt range");
     using T = uint16_t;
     using SAcc = f32x16[KBW][NQ];
+    using PAcc = u32x4[NQ][KBW][2];
 
     __shared__ __align__(16) unsigned char smem[LDS_B];
 
@@ -142,6 +160,7 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
     const int hh = lane >> 5;
 
     // ---- which (batch, head, query tile) ---------------------------------
+    constexpr int BM = 4 * 32 * NQ;
     const int G = gridDim.x;
     const int g = blockIdx.x;
     const int w = p.remap ? (g & 7) * (G >> 3) + (g >> 3) : g;
@@ -163,12 +182,10 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
     T* op = static_cast<T*>(p.o) + b * p.sq.b + h * p.sq.h;
 
     const int qw0 = q0 + wq * 32 * NQ;  // first query row of this wave
-    const bool wave_active = qw0 < p.Sq;
-    const int wave_kend = p.causal ? min(nb, min(qw0 + 32 * NQ, p.Sq)) : nb;
+    // Waves past the last query row compute on zero queries and store nothing.
     const int wave_lim_min = p.causal ? min(nb, qw0 + 1) : nb;  // keys past this need masks
     // first key of this wave's part of `tile`
-    auto wkey0 = [&](int tile) { return tile * BN + kb0 * 32; };
-    auto active = [&](int tile) { return wave_active && wkey0(tile) < wave_kend; };
+    auto wkey0 = [&](int tile) __attribute__((always_inline)) { return tile * BN + kb0 * 32; };
 
     // ---- Q operands (B of S^T = K Q^T), in registers for the whole loop ----
     // K-step s holds q[row][16s + 8h .. +7].
@@ -200,7 +217,7 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
         voff[i] = row * p.sk.s + (pc ^ swz_v<D>(row)) * 8;
     }
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)smem;
-    auto issue_tile = [&](int tile) {
+    auto issue_tile = [&](int tile) __attribute__((always_inline)) {
         const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + (tile % NST) * STAGE_B + wave * 1024);
         const int key0 = tile * BN;
         if (key0 + BN <= nb) {
@@ -222,22 +239,21 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
             }
         }
     };
-    // wait until at most n_after tiles' DMA loads (issued after the awaited
-    // tile) are still in flight
-    auto wait_tiles = [&](int n_after) {
-        if constexpr (P >= 3) {
-            if (n_after >= 2) { wait_vmcnt<(P >= 3 ? 2 * DPT : 0)>(); return; }
-        }
-        if constexpr (P >= 2) {
-            if (n_after >= 1) { wait_vmcnt<(P >= 2 ? DPT : 0)>(); return; }
-        }
+    // Wait until this thread's DMA loads of `tile` have landed, given that
+    // tiles up to `last_issued` (at most tile + P - 2) were issued after it.
+    auto wait_tile = [&](int tile, int last_issued) __attribute__((always_inline)) {
+        const int after = last_issued - tile;
+        if constexpr (P - 2 >= 4) { if (after >= 4) { wait_vmcnt<((P - 2 >= 4) ? 4 * DPT : 0)>(); return; } }
+        if constexpr (P - 2 >= 3) { if (after >= 3) { wait_vmcnt<((P - 2 >= 3) ? 3 * DPT : 0)>(); return; } }
+        if constexpr (P - 2 >= 2) { if (after >= 2) { wait_vmcnt<((P - 2 >= 2) ? 2 * DPT : 0)>(); return; } }
+        if constexpr (P - 2 >= 1) { if (after >= 1) { wait_vmcnt<((P - 2 >= 1) ? DPT : 0)>(); return; } }
         wait_vmcnt<0>();
     };
 
     // ---- operand reads ----------------------------------------------------------
-    auto stage = [&](int tile) { return smem + (tile % NST) * STAGE_B; };
+    auto stage = [&](int tile) __attribute__((always_inline)) { return smem + (tile % NST) * STAGE_B; };
     // A operand of S^T for key block kb (of the tile), K-step s
-    auto k_operand = [&](const unsigned char* kt, int kb, int s) -> u32x4 {
+    auto k_operand = [&](const unsigned char* kt, int kb, int s) __attribute__((always_inline)) -> u32x4 {
         const int row = kb * 32 + n32;
         const int lc = 2 * s + hh;
         return *reinterpret_cast<const u32x4*>(kt + row * RB + ((lc ^ swz_k<D>(row)) << 4));
@@ -249,7 +265,7 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
     const int grp = lane >> 4;
     const int e_tr = (lane & 15) >> 2;
     const int q_tr = lane & 3;
-    auto v_operand = [&](const unsigned char* vt, int kb, int u, int db) -> u32x4 {
+    auto v_operand = [&](const unsigned char* vt, int kb, int u, int db) __attribute__((always_inline)) -> u32x4 {
         u32x2 part[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -261,233 +277,221 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
         }
         return u32x4{part[0][0], part[0][1], part[1][0], part[1][1]};
     };
+    // Operands are read LA product slots ahead of their first product: K
+    // operand o (K-step o / KBW, key block o % KBW) feeds products
+    // NPV + o*NQ .. +NQ-1 of an iteration, V operand o (key block, u, db in
+    // that order) feeds products o*NQ .. +NQ-1. V operands due in the first
+    // LA slots are read at the end of the previous iteration.
+    constexpr int NV = KBW * 2 * (D / 32);
+    constexpr int NK = KBW * (D / 16);
+    constexpr int LA = 4;
+    u32x4 kop[NK];
+    u32x4 vop[NV];
+    auto read_kop = [&](int o, const unsigned char* kt) __attribute__((always_inline)) {
+        kop[o] = k_operand(kt, kb0 + o % KBW, o / KBW);
+    };
+    auto read_vop = [&](int o, const unsigned char* vt) __attribute__((always_inline)) {
+        vop[o] = v_operand(vt + TILE_B, kb0 + o / (2 * (D / 32)), (o / (D / 32)) % 2, o % (D / 32));
+    };
+    // the V operands due in the first LA slots of the next iteration
+    auto read_v_carry = [&](int tile) __attribute__((always_inline)) {
+#pragma unroll
+        for (int f = 0; f < LA && f < NPV; ++f)
+            if (f % NQ == 0) read_vop(f / NQ, stage(tile));
+    };
 
     // ---- running state -----------------------------------------------------
+    // m_run: the reference max (log2 units, always finite); l_run: the sum of
+    // this lane's probabilities against it.
     f32x16 oacc[NQ][D / 32];
-    float m_run[NQ], l_run[NQ];
+    float m_run[NQ], l_run[NQ], l_old[NQ];
 #pragma unroll
     for (int gq = 0; gq < NQ; ++gq) {
-        m_run[gq] = kNegInf;
+        m_run[gq] = 0.f;
         l_run[gq] = 0.f;
+        l_old[gq] = 0.f;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[gq][db][r] = 0.f;
     }
     const float c = p.c;
+    SAcc s_buf[2];   // scores of tile t (softmax) and t+1 (being multiplied)
+    PAcc pq[2];      // probabilities of tile t (softmax) and t-1 (output product)
 
-    auto qk_tile = [&](const unsigned char* kt, SAcc& sacc) {
-#pragma unroll
-        for (int kb = 0; kb < KBW; ++kb)
-#pragma unroll
-            for (int gq = 0; gq < NQ; ++gq)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb][gq][r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-#pragma unroll
-            for (int kb = 0; kb < KBW; ++kb) {
-                const u32x4 a = k_operand(kt, kb0 + kb, s);
-#pragma unroll
-                for (int gq = 0; gq < NQ; ++gq) sacc[kb][gq] = mfma16<Tag>(a, qop[gq][s], sacc[kb][gq]);
-            }
-        }
+    // Product number i of K Q^T into S, order (s, kb, gq).
+    auto qk_mfma = [&](int i, SAcc& S) __attribute__((always_inline)) {
+        const int gq = i % NQ, kb = (i / NQ) % KBW, s = i / (NQ * KBW);
+        const f32x16 zero = {};
+        S[kb][gq] = mfma16<Tag>(kop[i / NQ], qop[gq][s], s == 0 ? zero : S[kb][gq]);
     };
-
-    // pq[gq][kb][u]: B operand of the (kb, u) product, the probabilities of
-    // result registers 8u .. 8u+7 rounded and packed in pairs
-    u32x4 pq[NQ][KBW][2];
-    // Softmax of one tile against a reference max m_run (log2 units): the
-    // probabilities are exp2(s c - m_run), rounded and packed for the second
-    // product, and summed. The exact row max is only taken when a row has no
-    // reference yet (its first tile) or when the tile's probabilities show the
-    // reference fell far behind (a probability above 2^32, or infinite): then
-    // m_run moves to the exact running max, l and O are rescaled by
-    // exp2(m_old - m_new) (O after the caller's join, through `rescale`), and
-    // the tile is redone. Any reference gives the same softmax; this one keeps
-    // every probability below 2^32 while skipping the max on almost all tiles.
-    auto softmax_tile = [&](auto masked_tag, SAcc& sacc, int tile, float (&alpha_out)[NQ], bool& rescale) {
-        constexpr bool MASKED = decltype(masked_tag)::value;
+    // Product number i of P V into O, order (kb, u, db, gq).
+    auto pv_mfma = [&](int i, const PAcc& Pm) __attribute__((always_inline)) {
+        const int gq = i % NQ, db = (i / NQ) % (D / 32), u = (i / (NQ * (D / 32))) % 2,
+                  kb = i / (NQ * (D / 32) * 2);
+        oacc[gq][db] = mfma16<Tag>(vop[i / NQ], Pm[gq][kb][u], oacc[gq][db]);
+    };
+    // Probability pair j of the lane: block (kb, gq) = ((j/8) % KBW, j / (8 KBW)),
+    // result registers r, r+1 with r = 2 (j % 8).
+    auto prob_pair = [&](int j, const SAcc& S, PAcc& Pm, float m, float& l) __attribute__((always_inline)) {
+        const int gq = j / (8 * KBW), kb = (j / 8) % KBW, r = 2 * (j % 8);
+        // masked scores are -inf and c > 0, so their probabilities are 0
+        const float p0 = fast_exp2(fmaf(S[kb][gq][r], c, -m));
+        const float p1 = fast_exp2(fmaf(S[kb][gq][r + 1], c, -m));
+        const uint32_t w2 = pack2<Tag>(p0, p1);
+        Pm[gq][kb][r / 8][(r / 2) & 3] = w2;
+        l = dot2_sum<Tag>(w2, l);
+    };
+    // Scores of `tile` past the rows' limits (causal, key length) -> -inf.
+    auto mask_scores = [&](SAcc& S, int tile) __attribute__((always_inline)) {
 #pragma unroll
         for (int gq = 0; gq < NQ; ++gq) {
-            if constexpr (MASKED) {
-                const int qi = qw0 + gq * 32 + n32;
-                const int lim = p.causal ? min(nb, qi + 1) : nb;
+            const int qi = qw0 + gq * 32 + n32;
+            const int lim = p.causal ? min(nb, qi + 1) : nb;
 #pragma unroll
-                for (int kb = 0; kb < KBW; ++kb)
+            for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (wkey0(tile) + kb * 32 + blk_row(r, hh) >= lim) sacc[kb][gq][r] = kNegInf;
-            }
-            // probabilities against reference m (pack + partial row sum)
-            auto exps = [&](float m) -> float {
-                const float m_use = (m == kNegInf) ? 0.f : m;
-                float rs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < KBW; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; r += 2) {
-                        const float x0 = sacc[kb][gq][r], x1 = sacc[kb][gq][r + 1];
-                        float p0 = fast_exp2(fmaf(x0, c, -m_use));
-                        float p1 = fast_exp2(fmaf(x1, c, -m_use));
-                        if constexpr (MASKED) {
-                            p0 = (x0 == kNegInf) ? 0.f : p0;
-                            p1 = (x1 == kNegInf) ? 0.f : p1;
-                        }
-                        const uint32_t w2 = pack2<Tag>(p0, p1);
-                        pq[gq][kb][r / 8][(r / 2) & 3] = w2;
-                        rs[(r / 2) & 3] = dot2_sum<Tag>(w2, rs[(r / 2) & 3]);
-                    }
-                return (rs[0] + rs[1]) + (rs[2] + rs[3]);
-            };
-            alpha_out[gq] = 1.f;
-            float rs_tile = 0.f;
-            // at most two passes: the second only after the reference moved
-            for (int pass = 0; pass < 2; ++pass) {
-                rs_tile = exps(m_run[gq]);
-                if (!__any(m_run[gq] == kNegInf || !(rs_tile <= kRefGuard))) break;
-                // row max: four independent max3 chains, then the other lane half
-                float mq[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-#pragma unroll
-                for (int kb = 0; kb < KBW; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; r += 4) {
-                        const int ch = (kb * 4 + r / 4) & 3;
-                        mq[ch] = fmaxf(mq[ch], fmaxf(sacc[kb][gq][r], sacc[kb][gq][r + 1]));
-                        mq[ch] = fmaxf(mq[ch], fmaxf(sacc[kb][gq][r + 2], sacc[kb][gq][r + 3]));
-                    }
-                float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-                mx = fmaxf(mx, swap_halves(mx));
-                const float mxs = (MASKED && mx == kNegInf) ? kNegInf : mx * c;
-                const float m_new = fmaxf(m_run[gq], mxs);
-                const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run[gq] - m_new);
-                m_run[gq] = m_new;
-                l_run[gq] *= alpha;
-                alpha_out[gq] *= alpha;
-                rescale = true;
-                if (m_new == kNegInf) break;  // every key of the row masked so far: p = 0
-            }
-            l_run[gq] += rs_tile;
+                for (int r = 0; r < 16; ++r)
+                    if (wkey0(tile) + kb * 32 + blk_row(r, hh) >= lim) S[kb][gq][r] = kNegInf;
         }
     };
-
-    auto pv_tile = [&](const unsigned char* vt) {
+    // Block gq after a sum left the range: move the reference to the exact
+    // running max, rescale l (O by the caller, with the returned factor) and
+    // redo the probabilities. Both lane halves of a query decide alike.
+    auto exact_max = [&](int gq, const SAcc& S, PAcc& Pm) __attribute__((always_inline)) -> float {
+        float mq[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
         for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int r = 0; r < 16; r += 4) {
+                const int ch = (kb * 4 + r / 4) & 3;
+                mq[ch] = fmaxf(mq[ch], fmaxf(S[kb][gq][r], S[kb][gq][r + 1]));
+                mq[ch] = fmaxf(mq[ch], fmaxf(S[kb][gq][r + 2], S[kb][gq][r + 3]));
+            }
+        float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+        mx = fmaxf(mx, swap_halves(mx));
+        const float mxs = mx * c;  // -inf stays -inf (c > 0)
+        const float l_row_old = l_old[gq] + swap_halves(l_old[gq]);
+        // nothing accumulated yet: the old reference carries no weight
+        float m_new = l_row_old > 0.f ? fmaxf(m_run[gq], mxs) : mxs;
+        if (m_new == kNegInf) m_new = m_run[gq];  // every key of the row masked so far
+        const float alpha = l_row_old > 0.f ? fast_exp2(m_run[gq] - m_new) : 1.f;
+        m_run[gq] = m_new;
+        float l = l_old[gq] * alpha;
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const u32x4 a = v_operand(vt, kb0 + kb, u, db);
+        for (int j = 0; j < 8 * KBW; ++j) prob_pair(gq * 8 * KBW + j, S, Pm, m_new, l);
+        l_run[gq] = l;
+        return alpha;
+    };
+    // After the probabilities of a tile (and the products of the previous
+    // one): blocks with a sum out of range take the exact-max path, and their
+    // O is rescaled.
+    auto fix_range = [&](const SAcc& S, PAcc& Pm) __attribute__((always_inline)) {
+        // one test over all blocks first: every block's sum is then needed
+        // before any branch, which keeps the probability work in place
+        bool bad = false;
 #pragma unroll
-                    for (int gq = 0; gq < NQ; ++gq) oacc[gq][db] = mfma16<Tag>(a, pq[gq][kb][u], oacc[gq][db]);
-                }
+        for (int gq = 0; gq < NQ; ++gq) bad = bad || sum_out_of_range(l_run[gq]);
+        if (__builtin_amdgcn_ballot_w64(bad) == 0) return;
+#pragma unroll
+        for (int gq = 0; gq < NQ; ++gq) {
+            if (__builtin_amdgcn_ballot_w64(sum_out_of_range(l_run[gq])) == 0) continue;
+            const float alpha = exact_max(gq, S, Pm);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[gq][db][r] *= alpha;
+        }
     };
 
-    // softmax of tile t with the lazy rescale of O (applied after the masked /
-    // unmasked paths join: one place that changes O outside the products
-    // keeps O in fixed registers)
-    auto softmax_step = [&](int t, SAcc& s_now) {
-        float alpha[NQ];
-        bool rescale = false;
-        if (wkey0(t) + KBW * 32 > wave_lim_min)
-            softmax_tile(std::true_type{}, s_now, t, alpha, rescale);
-        else
-            softmax_tile(std::false_type{}, s_now, t, alpha, rescale);
-        if (rescale) {
+    // ---- the key loop ---------------------------------------------------------
+    // Iteration t (tile t's probabilities): wait for tile t+1, barrier, issue
+    // the DMA of tile t+P into the stage of tile t-2 (its last reads completed
+    // before the products of iteration t-1), read K(t+1); mask tile t's scores
+    // where some row cannot see all its keys; then the products P(t-1) V(t-1)
+    // and K(t+1) Q^T, one at a time, each followed by its share of tile t's
+    // probabilities; check the sums; read V(t) for the next iteration.
+    // At t = 0 the output product multiplies zero probabilities; at the last
+    // tile the score product reads a stale stage and its result is unused.
+    auto iteration = [&](auto par, int t) __attribute__((always_inline)) {
+        constexpr int B = decltype(par)::value;
+        SAcc& s_cur = s_buf[B];
+        SAcc& s_nxt = s_buf[B ^ 1];
+        PAcc& p_cur = pq[B];
+        PAcc& p_prv = pq[B ^ 1];
+        if (t + 1 < ntiles) wait_tile(t + 1, min(t + P - 1, ntiles - 1));
+        barrier_nofence();
+        if (t + P < ntiles) issue_tile(t + P);
+        const unsigned char* kt = stage(t + 1);
+        const unsigned char* vt = stage(t > 0 ? t - 1 : 0);
+        if (wkey0(t) + KBW * 32 > wave_lim_min) mask_scores(s_cur, t);
+        float l[NQ];
 #pragma unroll
-            for (int gq = 0; gq < NQ; ++gq)
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[gq][db][r] *= alpha[gq];
+        for (int gq = 0; gq < NQ; ++gq) {
+            l_old[gq] = l_run[gq];
+            l[gq] = l_run[gq];
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            // operand reads for slot i + LA
+            const int f = i + LA;
+            if (f < NPV && f % NQ == 0) read_vop(f / NQ, vt);
+            if (f >= NPV && f < NM && (f - NPV) % NQ == 0) read_kop((f - NPV) / NQ, kt);
+            if (i < LA && i >= NPV && (i - NPV) % NQ == 0) read_kop((i - NPV) / NQ, kt);
+            if (i < NPV) pv_mfma(i, p_prv); else qk_mfma(i - NPV, s_nxt);
+#pragma unroll
+            for (int j = i * NPAIR / NM; j < (i + 1) * NPAIR / NM; ++j) {
+                const int gq = j / (8 * KBW);
+                prob_pair(j, s_cur, p_cur, m_run[gq], l[gq]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int gq = 0; gq < NQ; ++gq) l_run[gq] = l[gq];
+        fix_range(s_cur, p_cur);
+        read_v_carry(t);
     };
 
-    if constexpr (KSPLIT == 2) {
-        // ---- ping-pong key loop --------------------------------------------------
-        // Per wave: M(t) = {O += P(t-1) V(t-1); S(t) = K(t) Q^T} on the matrix
-        // cores, then V(t) = softmax of S(t) on the vector units. Both wave
-        // groups run the same loop, [barrier] M(i) [barrier] V(i), but group 1
-        // passes one extra barrier first (and group 0 one extra last), so group 1
-        // runs half an iteration behind: on every SIMD one wave issues products
-        // (at raised priority) while the other computes its softmax. Counting
-        // workgroup barriers g = 0, 1, ...: group 0 runs M(i) after g = 2i,
-        // group 1 after g = 2i+1. Tile t sits in stage t % 4: every wave waits
-        // for its own part of it before g = 2t, and it is issued after
-        // g = 2t-4, once both groups have finished M(t-3), the last reader of
-        // tile t-4 in that stage.
-        static_assert(NST == 4, "the ping-pong ring has four stages");
-        auto wait_tile = [&](int t) {  // tiles issued after t by now: t+1 at most
-            if (t + 1 < ntiles) wait_vmcnt<DPT>(); else wait_vmcnt<0>();
-        };
-        auto sync = [&]() {
-            __builtin_amdgcn_sched_barrier(0);
-            barrier_nofence();
-            __builtin_amdgcn_sched_barrier(0);
-        };
-        for (int t = 0; t < min(2, ntiles); ++t) issue_tile(t);
-        if (kh == 1) {  // g = 0
-            if (ntiles > 0) wait_tile(0);
-            sync();
-            if (2 < ntiles) issue_tile(2);
-        }
-        for (int i = 0; i <= ntiles; ++i) {
-            if (kh == 0 && i < ntiles) wait_tile(i);
-            sync();  // group 0: g = 2i, group 1: g = 2i+1
-            if (kh == 0 && i + 2 < ntiles) issue_tile(i + 2);
-            SAcc s_cur;
-            __builtin_amdgcn_s_setprio(1);
-            if (i >= 1 && active(i - 1)) pv_tile(stage(i - 1) + TILE_B);
-            if (i < ntiles && active(i)) qk_tile(stage(i), s_cur);
-            __builtin_amdgcn_s_setprio(0);
-            if (kh == 1 && i + 1 < ntiles) wait_tile(i + 1);
-            sync();  // group 0: g = 2i+1, group 1: g = 2i+2
-            if (kh == 1 && i + 3 < ntiles) issue_tile(i + 3);
-            if (i < ntiles && active(i)) softmax_step(i, s_cur);
-        }
-        if (kh == 0) sync();  // g = 2*ntiles + 2
-    } else {
-        // ---- key loop over the DMA ring ---------------------------------------------
-        // Unrolled by two so the score registers of tiles t and t+1 alternate
-        // between two fixed sets instead of being copied.
-        constexpr int AHEAD = PIPE ? 1 : 0;  // tiles needed beyond the one softmaxed
-        auto step = [&](int t, SAcc& s_now, SAcc& s_nxt) {
-            const int last_issued = min(t + P - 1, ntiles - 1);
-            const int need = min(t + AHEAD, ntiles - 1);
-            wait_tiles(last_issued - need);
-            barrier_nofence();  // tiles <= need are in LDS; every wave is done with tile t-1
-            if (t + P < ntiles) issue_tile(t + P);  // into the stage of tile t-1
-            if constexpr (PIPE) {
-                if (t + 1 < ntiles && active(t + 1)) qk_tile(stage(t + 1), s_nxt);
-            } else {
-                if (active(t)) qk_tile(stage(t), s_now);
-            }
-            if (active(t)) {
-                softmax_step(t, s_now);
-                pv_tile(stage(t) + TILE_B);
-            }
-        };
-        SAcc s_a, s_b;
-        const int first = min(P, ntiles);
-        for (int t = 0; t < first; ++t) issue_tile(t);
-        if constexpr (PIPE) {
-            if (ntiles > 0) {
-                wait_tiles(first - 1);
-                barrier_nofence();
-                if (active(0)) qk_tile(stage(0), s_a);
-            }
-        }
-        for (int t = 0; t < ntiles; t += 2) {
-            step(t, s_a, s_b);
-            if (t + 1 < ntiles) step(t + 1, s_b, s_a);
+    for (int t = 0; t < min(P, ntiles); ++t) issue_tile(t);
+    if (ntiles > 0) {
+        wait_tile(0, min(P, ntiles) - 1);
+        barrier_nofence();
+#pragma unroll
+        for (int o = 0; o < NK; ++o) read_kop(o, stage(0));
+#pragma unroll
+        for (int i = 0; i < NQK; ++i) qk_mfma(i, s_buf[0]);
+        read_v_carry(0);
+#pragma unroll
+        for (int gq = 0; gq < NQ; ++gq)
+#pragma unroll
+            for (int kb = 0; kb < KBW; ++kb) pq[1][gq][kb][0] = pq[1][gq][kb][1] = u32x4{0u, 0u, 0u, 0u};
+    }
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+        iteration(int_c<0>{}, t);
+        iteration(int_c<1>{}, t + 1);
+    }
+    if (t < ntiles) iteration(int_c<0>{}, t);
+    if (ntiles > 0) {
+        // products of the last tile (its first V operands came with the carry)
+#pragma unroll
+        for (int o = 0; o < NV; ++o)
+            if (o * NQ >= LA) read_vop(o, stage(ntiles - 1));
+        if ((ntiles - 1) & 1) {
+#pragma unroll
+            for (int i = 0; i < NPV; ++i) pv_mfma(i, pq[1]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NPV; ++i) pv_mfma(i, pq[0]);
         }
     }
     __syncthreads();  // all DMA landed (last wait was vmcnt(0)) and all reads done
 
     // ---- merge the two key halves (KSPLIT = 2) ------------------------------
     // Lane (n32, h) of waves w and w+4 holds the same queries and the same
-    // rows of O^T over disjoint keys: O = O_a 2^(m_a - m) + O_b 2^(m_b - m).
+    // rows of O^T over disjoint keys: O = O_a 2^(m_a - m) + O_b 2^(m_b - m),
+    // where a half with nothing accumulated (l = 0) has no weight.
     if constexpr (KSPLIT == 2) {
         float* mrg = reinterpret_cast<float*>(smem) + wq * (MRG_W / 4);
         if (kh == 1) {
@@ -507,9 +511,12 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
             for (int gq = 0; gq < NQ; ++gq) {
                 const float mb = mrg[(NQ * (D / 32) * 16 + 2 * gq) * 64 + lane];
                 const float lb = mrg[(NQ * (D / 32) * 16 + 2 * gq + 1) * 64 + lane];
-                const float mm = fmaxf(m_run[gq], mb);
-                const float mu = (mm == kNegInf) ? 0.f : mm;
-                const float wa = fast_exp2(m_run[gq] - mu), wb = fast_exp2(mb - mu);
+                // both lane halves of a query decide alike: use the row sums
+                const float la_row = l_run[gq] + swap_halves(l_run[gq]);
+                const float lb_row = lb + swap_halves(lb);
+                const float mm = la_row == 0.f ? mb : (lb_row == 0.f ? m_run[gq] : fmaxf(m_run[gq], mb));
+                const float wa = la_row == 0.f ? 0.f : fast_exp2(m_run[gq] - mm);
+                const float wb = lb_row == 0.f ? 0.f : fast_exp2(mb - mm);
                 m_run[gq] = mm;
                 l_run[gq] = l_run[gq] * wa + lb * wb;
 #pragma unroll
@@ -558,7 +565,7 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
     }
 }
 
-template <typename Tag, int D, int NQ, int BN, int NST, bool PIPE, int KSPLIT>
+template <typename Tag, int D, int NQ, int BN, int NST, int KSPLIT>
 hipError_t launch16(const FwdArgs& a, hipStream_t stream) {
     constexpr int BM = 4 * 32 * NQ;
     Prefill16Params p;
@@ -574,13 +581,15 @@ hipError_t launch16(const FwdArgs& a, hipStream_t stream) {
     p.H = a.H;
     p.Sq = a.Sq;
     p.Sk = a.Sk;
-    p.c = a.scale * kLog2e;
+    // c > 0 keeps masked scores (-inf) at probability 0; scale 0 becomes the
+    // limit scale -> 0+, the same uniform attention
+    p.c = a.scale > 0.f ? a.scale * kLog2e : 1e-30f;
     p.causal = a.causal ? 1 : 0;
     p.n_qtiles = (a.Sq + BM - 1) / BM;
     const int64_t grid = (int64_t)p.n_qtiles * a.B * a.H;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     p.remap = (grid % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((fwd_prefill16_kernel<Tag, D, NQ, BN, NST, PIPE, KSPLIT>), dim3((unsigned)grid), dim3(256 * KSPLIT), 0,
+    hipLaunchKernelGGL((fwd_prefill16_kernel<Tag, D, NQ, BN, NST, KSPLIT>), dim3((unsigned)grid), dim3(256 * KSPLIT), 0,
                        stream, p);
     return hipGetLastError();
 }
@@ -588,20 +597,19 @@ hipError_t launch16(const FwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 // Kernel choice (measured on MI355X): head size 64 over long key ranges uses
-// the 8-wave ping-pong kernel (half the LDS operand traffic per product and
-// products of one group overlapping the other group's softmax); short key
-// ranges, where its pipeline fill and final merge do not pay off, and head
-// size 128 use the 4-wave pipelined kernel.
-constexpr int kPingPongMinKeys = 2048;
+// 8 waves in two key halves (half the LDS operand traffic per product);
+// short key ranges, where the longer pipeline fill and the final merge do not
+// pay off, and head size 128 use 4 waves.
+constexpr int kKeySplitMinKeys = 2048;
 
 hipError_t run_prefill16(const FwdArgs& a, hipStream_t stream) {
-    const bool pp = a.d == 64 && a.Sk >= kPingPongMinKeys;
+    const bool ks = a.d == 64 && a.Sk >= kKeySplitMinKeys;
     if (a.dtype == 2) {
-        if (a.d == 128) return launch16<BF16, 128, 1, 32, 4, true, 1>(a, stream);
-        return pp ? launch16<BF16, 64, 2, 64, 4, true, 2>(a, stream) : launch16<BF16, 64, 1, 64, 4, true, 1>(a, stream);
+        if (a.d == 128) return launch16<BF16, 128, 1, 32, 5, 1>(a, stream);
+        return ks ? launch16<BF16, 64, 2, 64, 8, 2>(a, stream) : launch16<BF16, 64, 1, 64, 5, 1>(a, stream);
     }
-    if (a.d == 128) return launch16<F16, 128, 1, 32, 4, true, 1>(a, stream);
-    return pp ? launch16<F16, 64, 2, 64, 4, true, 2>(a, stream) : launch16<F16, 64, 1, 64, 4, true, 1>(a, stream);
+    if (a.d == 128) return launch16<F16, 128, 1, 32, 5, 1>(a, stream);
+    return ks ? launch16<F16, 64, 2, 64, 8, 2>(a, stream) : launch16<F16, 64, 1, 64, 5, 1>(a, stream);
 }
 
 }  // namespace attn
