@@ -98,7 +98,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--config", default="medium_bf16")
     ap.add_argument("--path", default="fused", choices=["fused", "naive", "splitk"])
     ap.add_argument("--n-split", type=int, default=None)

@@ -187,21 +187,9 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
     // first key of this wave's part of `tile`
     auto wkey0 = [&](int tile) __attribute__((always_inline)) { return tile * BN + kb0 * 32; };
 
-    // ---- Q operands (B of S^T = K Q^T), in registers for the whole loop ----
-    // K-step s holds q[row][16s + 8h .. +7].
+    // Q operands (B of S^T = K Q^T), in registers for the whole loop: K-step
+    // s holds q[row][16s + 8h .. +7]. Loaded with the first DMA tile below.
     u32x4 qop[NQ][D / 16];
-#pragma unroll
-    for (int gq = 0; gq < NQ; ++gq) {
-        const int qi = qw0 + gq * 32 + n32;
-        const bool ok = qi < p.Sq;
-        const T* row = qp + (int64_t)(ok ? qi : 0) * p.sq.s;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            qop[gq][s] = ok ? *reinterpret_cast<const u32x4*>(row + s * 16 + hh * 8) : z;
-        }
-    }
-    wait_vmcnt<0>();  // Q is in registers before any DMA load is in flight
 
     // ---- DMA of one K/V tile into LDS stage tile % NST ----------------------
     // Thread-slot i*NT + tid of the tile is the 16-byte chunk (row, pc); it
@@ -340,7 +328,7 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
         const float p1 = fast_exp2(fmaf(S[kb][gq][r + 1], c, -m));
         const uint32_t w2 = pack2<Tag>(p0, p1);
         Pm[gq][kb][r / 8][(r / 2) & 3] = w2;
-        l = dot2_sum<Tag>(w2, l);
+        l = dot2_sum<Tag>(w2, l);  // the row sum uses the rounded probabilities
     };
     // Scores of `tile` past the rows' limits (causal, key length) -> -inf.
     auto mask_scores = [&](SAcc& S, int tile) __attribute__((always_inline)) {
@@ -453,9 +441,24 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
         read_v_carry(t);
     };
 
-    for (int t = 0; t < min(P, ntiles); ++t) issue_tile(t);
+    // Tile 0 and the Q operands load together (one wait covers both); the
+    // rest of the ring goes out after it.
+    if (ntiles > 0) issue_tile(0);
+    // ---- Q operands (B of S^T = K Q^T), in registers for the whole loop ----
+#pragma unroll
+    for (int gq = 0; gq < NQ; ++gq) {
+        const int qi = qw0 + gq * 32 + n32;
+        const bool ok = qi < p.Sq;
+        const T* row = qp + (int64_t)(ok ? qi : 0) * p.sq.s;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            qop[gq][s] = ok ? *reinterpret_cast<const u32x4*>(row + s * 16 + hh * 8) : z;
+        }
+    }
+    wait_vmcnt<0>();
+    for (int t = 1; t < min(P, ntiles); ++t) issue_tile(t);
     if (ntiles > 0) {
-        wait_tile(0, min(P, ntiles) - 1);
         barrier_nofence();
 #pragma unroll
         for (int o = 0; o < NK; ++o) read_kop(o, stage(0));
