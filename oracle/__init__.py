@@ -14,7 +14,8 @@ its citations of the pages, is in that C file:
 * the per-element online recurrence: page "[Performance] [WebGPU] Proposal:
   Add an option to use online softmax instead of naive softmax", §四;
 * the (m, l) block merge: page "WebGPU 算子优化：QKV 内存合并与 FlashAttention
-  分块计算", section "FlashAttention 分块计算原理与浏览器适配".
+  分块计算", section "FlashAttention 分块计算原理与浏览器适配";
+* the QKV projection against the concatenated weight: the chapter's §2.1.
 
 Inputs are torch CPU tensors (float32, float16, bfloat16) or numpy arrays
 (float32, float16) in layout "bhsd" = [B, H, S, d] or "bshd" = [B, S, H, d].
@@ -62,6 +63,9 @@ class Oracle:
         lib.oracle_online_softmax.restype = None
         lib.oracle_merge.argtypes = [_c_i64, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp, _c_vp]
         lib.oracle_merge.restype = None
+        lib.oracle_qkv_proj.argtypes = [_c_vp, _c_vp, _c_int, _c_int, _c_i64, _c_i64, _c_i64,
+                                        _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_int]
+        lib.oracle_qkv_proj.restype = _c_int
         lib.oracle_decode.argtypes = [_c_vp, _c_i64, _c_int]
         lib.oracle_decode.restype = _c_dbl
         self.lib = lib
@@ -197,6 +201,25 @@ class Oracle:
                                        p.ctypes.data)
         return mt, lt, p
 
+    def qkv_proj(self, x, w, *, H, d, layout="bhsd", nthreads=None):
+        """QKV projection by definition: x [B, S, D], w [3*H*d, D] (out-major).
+        Returns (q, k, v) float64 in `layout` ([B,H,S,d] or [B,S,H,d])."""
+        B, S, D = (int(n) for n in x.shape)
+        if tuple(w.shape) != (3 * H * d, D):
+            raise ValueError(f"w must have shape [3*H*d, D] = {(3 * H * d, D)}")
+        xa, xp, xc = self._buffer(x)
+        wa, wp, wc = self._buffer(w)
+        if xc != wc:
+            raise TypeError("x and w must share one dtype")
+        shape = (B, H, S, d) if layout == "bhsd" else (B, S, H, d)
+        outs = [np.empty(shape, dtype=np.float64) for _ in range(3)]
+        rc = self.lib.oracle_qkv_proj(xp, wp, xc, _LAYOUT_CODES[layout], B, S, D, H, d,
+                                      *(o.ctypes.data for o in outs), self._threads(nthreads))
+        if rc:
+            raise RuntimeError(f"oracle_qkv_proj failed with code {rc}")
+        del xa, wa
+        return tuple(outs)
+
     def decode(self, x):
         """Every element of x decoded to float64 by the oracle's own reader."""
         keep, ptr, code = self._buffer(x)
@@ -240,3 +263,7 @@ def online_softmax(*a, **kw):
 
 def decode(*a, **kw):
     return default().decode(*a, **kw)
+
+
+def qkv_proj(*a, **kw):
+    return default().qkv_proj(*a, **kw)

@@ -21,6 +21,11 @@
  *   [Blog] "WebGPU 算子优化：QKV 内存合并与 FlashAttention 分块计算"
  *            section "FlashAttention 分块计算原理与浏览器适配": merging the
  *            (m, l) statistics of separate key blocks (test aid)
+ *            section "QKV 矩阵的内存合并模式选择": Q, K, V of all heads, each
+ *            in its own buffer of B x S x heads x d elements
+ *   [Ch2]  §2.1  the Q, K, V projections X W_Q, X W_K, X W_V, computed as one
+ *                product with the three weight matrices side by side and
+ *                then split
  *
  * The oracle is the plain definition, not the tiled method: for every query
  * row it materialises the whole score row over the valid keys, then runs the
@@ -339,4 +344,37 @@ void oracle_merge(int64_t n, const double* m, const double* l, const double* o, 
     }
     for (int64_t c = 0; c < d; ++c) o_out[c] /= lt;
     *lse_out = mx + log(lt);
+}
+
+/*
+ * QKV projection, [Ch2] §2.1 by definition: for t = 0, 1, 2 (Q, K, V),
+ *   out_t[b, h, s, c] = sum_i x[b, s, i] * W[i, t*H*d + h*d + c]
+ * where W = [W_Q | W_K | W_V] is the D x 3Hd concatenated weight. The weight
+ * is passed out-major, w[n * D + i] = W[i, n] (n = t*H*d + h*d + c), the
+ * usual storage of a linear layer's weight. x is [B, S, D] row-major; the
+ * three outputs are written in `layout` ([B,H,S,d] or [B,S,H,d]) as fp64.
+ * Returns 0, or 1 on bad sizes.
+ */
+int oracle_qkv_proj(const void* x, const void* w, int dtype, int layout, int64_t B, int64_t S,
+                    int64_t D, int64_t H, int64_t d, double* q, double* k, double* v,
+                    int nthreads) {
+    if (B < 0 || S < 0 || D < 1 || H < 1 || d < 1) return 1;
+    if (layout != ORC_BHSD && layout != ORC_BSHD) return 1;
+    double* outs[3] = {q, k, v};
+    const int64_t HD = H * d;
+    (void)nthreads;
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t bs = 0; bs < B * S; ++bs) {
+        const int64_t b = bs / S, s_ = bs % S;
+        for (int t = 0; t < 3; ++t)
+            for (int64_t h = 0; h < H; ++h)
+                for (int64_t c = 0; c < d; ++c) {
+                    const int64_t n = t * HD + h * d + c;
+                    double acc = 0.0;
+                    for (int64_t i = 0; i < D; ++i)
+                        acc += load(x, bs * D + i, dtype) * load(w, n * D + i, dtype);
+                    outs[t][at(layout, H, S, d, b, h, s_, c)] = acc;
+                }
+    }
+    return 0;
 }

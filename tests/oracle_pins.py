@@ -13,7 +13,8 @@ Sources of the facts (pages cited by title and section):
   page "[Performance] [WebGPU] Proposal: Add an option to use online softmax
     instead of naive softmax", §四 repro row, §七 numeric test;
   page "WebGPU 算子优化：QKV 内存合并与 FlashAttention 分块计算", section
-    "FlashAttention 分块计算原理与浏览器适配": block merge of (m, l).
+    "FlashAttention 分块计算原理与浏览器适配": block merge of (m, l);
+  the chapter's §2.1: Q, K, V as one product with the concatenated weight.
 """
 from __future__ import annotations
 
@@ -446,6 +447,51 @@ def pin_rows_api(orc):
             close(lrow[n], lse[b, h, i], 0.0, "rows API LSE")
 
 
+
+def _qkv_split(x64, w64, H, d, layout):
+    """numpy reference of the projection: y = x w^T, columns split into
+    (t, h, c) = (Q/K/V, head, dim), arranged in `layout`."""
+    B, S, _ = x64.shape
+    y = np.einsum("bsi,ni->bsn", x64, w64).reshape(B, S, 3, H, d)
+    outs = []
+    for t in range(3):
+        yt = y[:, :, t]                      # [B, S, H, d]
+        outs.append(yt if layout == "bshd" else np.transpose(yt, (0, 2, 1, 3)))
+    return outs
+
+
+def pin_qkv_identity(orc):
+    """With D = H*d and the concatenated weight [I | 2I | 3I] the projections
+    are x, 2x and 3x, each cut into heads of d consecutive columns: this fixes
+    the order Q, K, V, the head split and both output layouts exactly."""
+    rng = np.random.default_rng(21)
+    for layout in ("bhsd", "bshd"):
+        for (B, S, H, d) in [(2, 3, 2, 4), (1, 5, 3, 2)]:
+            D_ = H * d
+            x = rng.integers(-8, 9, size=(B, S, D_)).astype(np.float32)
+            w = np.concatenate([np.eye(D_) * (t + 1) for t in range(3)]).astype(np.float32)
+            q, k, v = orc.qkv_proj(x, w, H=H, d=d, layout=layout)
+            heads = x.reshape(B, S, H, d)
+            want = heads if layout == "bshd" else np.transpose(heads, (0, 2, 1, 3))
+            for t, got in enumerate((q, k, v)):
+                assert np.array_equal(got, (t + 1) * want), f"qkv identity {layout} output {t}"
+
+
+def pin_qkv_library(orc):
+    """Library cross-check: numpy's einsum of x with the weight, in float64,
+    for random inputs in every storage type and both layouts."""
+    rng = np.random.default_rng(22)
+    for layout in ("bhsd", "bshd"):
+        for dt in (torch.float32, torch.float16, torch.bfloat16):
+            B, S, D_, H, d = 2, 7, 24, 3, 4
+            x = torch.from_numpy(rand(rng, (B, S, D_))).to(dt)
+            w = torch.from_numpy(rand(rng, (3 * H * d, D_))).to(dt)
+            got = orc.qkv_proj(x, w, H=H, d=d, layout=layout)
+            want = _qkv_split(f64(x), f64(w), H, d, layout)
+            for t in range(3):
+                close(got[t], want[t], 1e-12, f"qkv vs einsum {layout} {dt} output {t}")
+
+
 ALL_PINS = [
     pin_decode_exact,
     pin_rows_sum_to_one,
@@ -461,4 +507,6 @@ ALL_PINS = [
     pin_torch_sdpa,
     pin_empty_rows,
     pin_rows_api,
+    pin_qkv_identity,
+    pin_qkv_library,
 ]

@@ -35,6 +35,11 @@ MUTANTS = {
         "                acc += a[j] *",
         "for (int64_t j = 0; j + 1 < p->Sk; ++j)\n            if (key_valid(p, nb, i, j))\n"
         "                acc += a[j] *"),
+    "qkv weight read in-major": ("load(w, n * D + i, dtype)", "load(w, i * 3 * HD + n, dtype)"),
+    "qkv outputs rotated": ("double* outs[3] = {q, k, v};", "double* outs[3] = {k, v, q};"),
+    "qkv heads interleaved": ("const int64_t n = t * HD + h * d + c;", "const int64_t n = t * HD + c * H + h;"),
+    "qkv drops last input": ("for (int64_t i = 0; i < D; ++i)\n                        acc +=",
+                             "for (int64_t i = 0; i + 1 < D; ++i)\n                        acc +="),
 }
 
 
