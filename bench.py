@@ -94,13 +94,85 @@ def cpu_baseline(w, t, target_s: float = 12.0):
                       f"{dt:.1f} s wall on {cores} threads (fp64, three-step softmax)"}
 
 
+def bench_qkv(args, w, torch, sdpa) -> int:
+    """QKV projection of the workload's tokens (model width D = H*d, the
+    weight [3*H*d, D]), alone or followed by the attention of the workload."""
+    from scaled_dot_product_flashattention_amd.inputs import generate_qkv_proj
+
+    B, S, H, d = w.B, w.Sq, w.H, w.d
+    D = H * d
+    dev = torch.device("cuda:0")
+    t = generate_qkv_proj(B, S, D, H, d, w.dtype, seed=w.seed)
+    x, wt = t["x"].to(dev), t["w"].to(dev)
+    shape = (B, H, S, d) if w.layout == "bhsd" else (B, S, H, d)
+    qkv = tuple(torch.empty(shape, dtype=x.dtype, device=dev) for _ in range(3))
+    o = torch.empty(shape, dtype=x.dtype, device=dev)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    proj_flops = 2.0 * B * S * (3 * H * d) * D
+    attn_flops = flops(w.replace(Sk=S, kv_len_range=None))
+    akw = dict(scale=w.scale, causal=w.causal, layout=w.layout, out=o, lse=lse)
+    if args.path == "qkv":
+        step = lambda: sdpa.attn_qkv_proj(x, wt, H=H, d=d, layout=w.layout, out=qkv)  # noqa: E731
+        fl = proj_flops
+    elif args.path == "qkv_attn":
+        def step():
+            q, k, v = sdpa.attn_qkv_proj(x, wt, H=H, d=d, layout=w.layout, out=qkv)
+            sdpa.attn_fwd(q, k, v, **akw)
+        fl = proj_flops + attn_flops
+    else:
+        wq, wk, wv = (wt[i * H * d:(i + 1) * H * d] for i in range(3))
+
+        def step():
+            outs = []
+            for wi in (wq, wk, wv):
+                y = torch.matmul(x, wi.t()).view(B, S, H, d)
+                outs.append(y.transpose(1, 2).contiguous() if w.layout == "bhsd" else y)
+            sdpa.attn_fwd(*outs, **akw)
+        fl = proj_flops + attn_flops
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tflops = fl / (ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS_16, "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_TFLOPS_16, 4), "traffic": None, "kernel_ms": round(ms, 5),
+            "algorithmic_units": "FLOPs per step", "algorithmic_per_launch": fl}
+    what = {"qkv": "QKV projection", "qkv_attn": "QKV projection + attention",
+            "qkv_attn_unfused": "unfused projections + attention"}[args.path]
+    line = {
+        "metric": f"{what} TFLOP/s, tokens of {w.description}, D={D}",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": {"f16": "fp16", "bf16": "bf16"}[w.dtype], "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "S": S, "D": D, "H": H, "d": d, "layout": w.layout,
+                   "causal": w.causal, "path": args.path, "flops_per_step": fl},
+        "roofline": roof,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--config", default="medium_bf16")
-    ap.add_argument("--path", default="fused", choices=["fused", "naive", "splitk"])
+    ap.add_argument("--path", default="fused",
+                    choices=["fused", "naive", "splitk", "qkv", "qkv_attn", "qkv_attn_unfused"],
+                    help="fused attention (default), the unfused baseline, the explicit "
+                         "split-K path, the QKV projection alone, projection + attention, "
+                         "or the unfused sequence (three library matmuls and layout "
+                         "copies, then attention)")
     ap.add_argument("--n-split", type=int, default=None)
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -123,6 +195,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     w = WORKLOADS[args.config]
+    if args.path.startswith("qkv"):
+        return bench_qkv(args, w, torch, sdpa)
     t = generate(w)
     dev = torch.device("cuda:0")
     q, k, v = (t[n].to(dev) for n in ("q", "k", "v"))

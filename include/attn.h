@@ -109,20 +109,42 @@ size_t attn_splitk_workspace_size(int B, int H, int Sq, int d, int n_split);
 
 /*
  * Unfused baseline with the materialised intermediates of the chapter's §2.5:
- * kernel 1 writes S = scale * Q K^T to scratch ([B, H, Sq, Sk], input type),
- * kernel 2 runs the three-step softmax on each row (max, then sum, then
- * normalise, each a pass over the stored row) and writes P (same shape and
- * type) plus LSE, kernel 3 computes O = P V. Same arguments and results as
- * attn_fwd; `scratch` must hold attn_naive_scratch_size bytes.
+ * kernel 1 writes S = scale * Q K^T to scratch ([B, H, Sq, Sk] in fp32, rows
+ * padded to a multiple of 64 keys), kernel 2 runs the three-step softmax on
+ * each row (max, then sum, then normalise, each a pass over the stored row)
+ * and writes P (same shape, input type) plus LSE, kernel 3 computes O = P V.
+ * Same arguments and results as attn_fwd; `scratch` must hold
+ * attn_naive_scratch_size bytes.
  */
 int attn_fwd_naive(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
                    int dtype, const int32_t* kv_len, void* scratch, size_t scratch_bytes,
                    void* stream);
 
-/* Scratch bytes for attn_fwd_naive: S and P, 2 * B*H*Sq*Sk elements of dtype,
- * plus alignment padding (0 for rejected arguments). Host only. */
+/* Scratch bytes for attn_fwd_naive: S in fp32 and P in dtype, B*H*Sq rows of
+ * Sk rounded up to 64 each (0 for rejected arguments). Host only. */
 size_t attn_naive_scratch_size(int B, int H, int Sq, int Sk, int dtype);
+
+/*
+ * QKV projection (§2.1 of the chapter: the three projections as one product
+ * with the weights side by side, then split). For t = 0, 1, 2 it writes
+ *     out_t[b, h, s, c] = sum_i x[b, s, i] * W[i, t*H*d + h*d + c]
+ * to out_0 = q, out_1 = k, out_2 = v, where W is the D x 3Hd concatenation
+ * [W_Q | W_K | W_V]. Storage:
+ *   x      [B, S, D] dense, element type `dtype`.
+ *   w      [3*H*d, D] dense: w[n*D + i] = W[i, n] (out-major, the storage of
+ *          a linear layer's weight), element type `dtype`.
+ *   q,k,v  [B, H, S, d] (ATTN_LAYOUT_BHSD) or [B, S, H, d] (ATTN_LAYOUT_BSHD),
+ *          dense, element type `dtype`: the inputs attn_fwd takes.
+ * dtype is ATTN_F16 or ATTN_BF16 (fp32 returns ATTN_E_UNSUPPORTED); products
+ * accumulate in fp32 and each output is rounded once (nearest-even).
+ * Requirements: B, S >= 1 (else ATTN_E_SHAPE); D a positive multiple of 64
+ * and d a positive multiple of 8 (else ATTN_E_SHAPE); B*S, 3*H*d and D each
+ * below 2^31; all pointers 16-byte aligned (ATTN_E_ALIGN); none NULL
+ * (ATTN_E_NULLPTR). Asynchronous on `stream` like attn_fwd; no workspace.
+ */
+int attn_qkv_proj(const void* x, const void* w, void* q, void* k, void* v, int B, int S, int D,
+                  int H, int d, int layout, int dtype, void* stream);
 
 /* Static text for a status code. */
 const char* attn_status_string(int status);

@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     attn_fwd_splitk,
     attn_fwd_workspace_size,
     attn_naive_scratch_size,
+    attn_qkv_proj,
     attn_splitk_workspace_size,
     attn_status_string,
     attn_version,

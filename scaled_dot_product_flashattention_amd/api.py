@@ -56,6 +56,8 @@ def load_library() -> ctypes.CDLL:
     L.attn_splitk_workspace_size.restype = sz
     L.attn_naive_scratch_size.argtypes = [i, i, i, i, i]
     L.attn_naive_scratch_size.restype = sz
+    L.attn_qkv_proj.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
+    L.attn_qkv_proj.restype = i
     L.attn_status_string.argtypes = [i]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_version.argtypes = []
@@ -207,3 +209,31 @@ def attn_fwd_naive(q, k, v, *, scale=None, causal=False, layout="bhsd", kv_len=N
     if rc:
         raise AttnError("attn_fwd_naive", rc)
     return o, lse
+
+
+def attn_qkv_proj(x, w, *, H, d, layout="bhsd", out=None, stream=None):
+    """QKV projection: x [B, S, D] and the out-major weight w [3*H*d, D] into
+    (q, k, v) in `layout`, the inputs of attn_fwd. `out` may supply the three
+    output tensors."""
+    for name, t in (("x", x), ("w", w)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if x.dim() != 3 or w.dim() != 2 or x.dtype != w.dtype:
+        raise ValueError("x must be [B, S, D] and w [3*H*d, D] of one dtype")
+    B, S, D = (int(n) for n in x.shape)
+    if tuple(w.shape) != (3 * H * d, D):
+        raise ValueError(f"w has shape {tuple(w.shape)}, expected {(3 * H * d, D)}")
+    shape = (B, H, S, d) if layout == "bhsd" else (B, S, H, d)
+    if out is None:
+        out = tuple(torch.empty(shape, dtype=x.dtype, device=x.device) for _ in range(3))
+    for t in out:
+        if tuple(t.shape) != shape or t.dtype != x.dtype or not t.is_contiguous():
+            raise ValueError("out tensors must be dense, of x's dtype and shape " + str(shape))
+    rc = load_library().attn_qkv_proj(_ptr(x), _ptr(w), *(_ptr(t) for t in out), B, S, D, int(H),
+                                      int(d), _LAYOUT[layout], dtype_code(x.dtype),
+                                      _stream(x, stream))
+    if rc:
+        raise AttnError("attn_qkv_proj", rc)
+    return tuple(out)

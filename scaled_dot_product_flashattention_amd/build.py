@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["attn_api.cpp", "fwd_prefill.hip", "fwd_prefill16.hip", "fwd_splitk.hip", "naive.hip"]
+SOURCES = ["attn_api.cpp", "fwd_prefill.hip", "fwd_prefill16.hip", "fwd_splitk.hip", "naive.hip",
+           "qkv_proj.hip"]
 ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
 
 

@@ -151,11 +151,36 @@ int attn_fwd_naive(const void* q, const void* k, const void* v, void* o, float* 
     return status_of(attn::run_naive(a, scratch, static_cast<hipStream_t>(stream)));
 }
 
+int attn_qkv_proj(const void* x, const void* w, void* q, void* k, void* v, int B, int S, int D,
+                  int H, int d, int layout, int dtype, void* stream) {
+    if (!x || !w || !q || !k || !v) return ATTN_E_NULLPTR;
+    if (layout != ATTN_LAYOUT_BHSD && layout != ATTN_LAYOUT_BSHD) return ATTN_E_UNSUPPORTED;
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
+    if (B < 1 || S < 1 || H < 1 || D < 64 || D % 64 != 0 || d < 8 || d % 8 != 0) return ATTN_E_SHAPE;
+    if ((int64_t)B * S > INT_MAX || (int64_t)3 * H * d > INT_MAX) return ATTN_E_SHAPE;
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+        return ATTN_E_ALIGN;
+    attn::QkvArgs a;
+    a.x = x;
+    a.w = w;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.B = B;
+    a.S = S;
+    a.D = D;
+    a.H = H;
+    a.d = d;
+    a.layout = layout;
+    a.dtype = dtype;
+    return status_of(attn::run_qkv_proj(a, static_cast<hipStream_t>(stream)));
+}
+
 const char* attn_status_string(int status) {
     switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_E_NULLPTR: return "a required pointer is NULL";
-    case ATTN_E_SHAPE: return "invalid shape: B, H, Sq, Sk and n_split must be >= 1 and sizes must fit";
+    case ATTN_E_SHAPE: return "invalid shape: sizes must be >= 1 (projection: D a multiple of 64, d of 8) and fit";
     case ATTN_E_UNSUPPORTED: return "unsupported head size (64 or 128), layout or dtype";
     case ATTN_E_ALIGN: return "misaligned pointer (tensors and workspaces 16 bytes, lse and kv_len 4 bytes)";
     case ATTN_E_WORKSPACE: return "workspace or scratch missing or too small";

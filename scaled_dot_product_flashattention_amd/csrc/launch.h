@@ -30,6 +30,19 @@ hipError_t run_prefill16(const FwdArgs& a, hipStream_t stream);
 size_t splitk_workspace_bytes(int B, int H, int Sq, int d, int n_split);
 hipError_t run_splitk(const FwdArgs& a, int n_split, void* workspace, hipStream_t stream);
 
+// QKV projection: x [B,S,D] times the out-major weight [3*H*d, D] into q, k, v.
+struct QkvArgs {
+    const void* x;
+    const void* w;
+    void* q;
+    void* k;
+    void* v;
+    int B, S, D, H, d;
+    int layout;  // 0 = [B,H,S,d], 1 = [B,S,H,d]
+    int dtype;   // 1 = fp16, 2 = bf16
+};
+hipError_t run_qkv_proj(const QkvArgs& a, hipStream_t stream);
+
 // Unfused three-kernel baseline.
 size_t naive_scratch_bytes(int B, int H, int Sq, int Sk, int dtype);
 hipError_t run_naive(const FwdArgs& a, void* scratch, hipStream_t stream);

@@ -1,0 +1,215 @@
+// Fused QKV projection for bf16 / fp16: one matrix product of the tokens
+// with the concatenated weight, written straight into Q, K and V.
+//
+// Method (chapter "2. 自注意力机制算子…以及FlashAttention优化", §2.1): the
+// projections X W_Q, X W_K and X W_V are done as one product with the three
+// weights side by side ([D, 3 Hd]) and then split. Here the split is part of
+// the store: output column n = t*Hd + h*d + c goes to tensor t (Q, K, V),
+// head h, dimension c, in the layout the attention kernel reads ([B,H,S,d] or
+// [B,S,H,d], page "WebGPU 算子优化…", section "QKV 矩阵的内存合并模式选择").
+//
+// Y = X W^T with X [M = B*S, K = D] and the weight stored out-major,
+// w[n][i] (as a linear layer keeps it), so both operands of the matrix
+// product are contiguous along the contraction.
+//
+// Mapping to gfx950:
+//   * 128 x 128 output tile per workgroup, 4 waves of 64 x 64 (2 x 2 blocks
+//     of 32 x 32). The products are computed transposed, Y^T = W X^T, on
+//     32x32x16 matrix-core blocks: A = weight rows, B = token rows.
+//   * K steps of 64: the 128 x 64 tiles of X and W go global -> LDS by
+//     direct DMA loads into a two-stage ring (one tile ahead), rows of 128 B
+//     with their 16-byte chunks XOR-swizzled so the ds_read_b128 operand
+//     reads are free of bank conflicts.
+//   * Epilogue: fp32 accumulators -> storage type (round to nearest even)
+//     -> LDS -> 16-byte stores, each chunk of 8 columns placed by (t, h, c).
+//   * Rows past M and columns past N reread the last valid row (finite) and
+//     are not stored.
+#include "device_common.h"
+#include "launch.h"
+
+namespace attn {
+
+namespace {
+
+constexpr int QBM = 128;  // token rows per workgroup
+constexpr int QBN = 128;  // output columns per workgroup
+constexpr int QBK = 64;   // contraction per stage
+constexpr int QNT = 256;  // threads
+constexpr int QROW = QBK * 2;               // bytes per LDS row
+constexpr int QTILE = QBM * QROW;           // bytes of one 128 x 64 tile
+constexpr int QSTAGE = 2 * QTILE;           // X tile, then W tile
+constexpr int QNST = 2;
+constexpr int QOROW = QBN + 8;              // output staging row (elements)
+
+typedef __attribute__((address_space(3))) void lds_void_q;
+
+struct QkvParams {
+    const void* x;
+    const void* w;
+    void* out[3];
+    int M, N, K;   // B*S, 3*H*d, D
+    int S, H, d;
+    int layout;    // 0 [B,H,S,d], 1 [B,S,H,d]
+    int n_ntiles;  // column tiles
+};
+
+template <int N> __device__ __forceinline__ void qwait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Direct global -> LDS load of 16 bytes per lane (see the attention kernel).
+__device__ __forceinline__ void qdma16(const void* src, uint32_t lds_addr) {
+    asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_addr) : "memory");
+}
+
+__device__ __forceinline__ void qbarrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// XOR swizzle of the 16-byte chunks of a 128-byte LDS row.
+__device__ __forceinline__ int qswz(int row) { return (row >> 1) & 7; }
+
+template <typename Tag>
+__global__ __launch_bounds__(QNT, 2) void qkv_proj_kernel(QkvParams p) {
+    using T = uint16_t;
+    __shared__ __align__(16) unsigned char smem[QNST * QSTAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1;  // 64-row half of the token rows
+    const int wn = wave & 1;   // 64-column half of the output columns
+    const int n32 = lane & 31;
+    const int hh = lane >> 5;
+
+    const int tm = blockIdx.x / p.n_ntiles;
+    const int tn = blockIdx.x - tm * p.n_ntiles;
+    const int m0 = tm * QBM, n0 = tn * QBN;
+
+    const T* xp = static_cast<const T*>(p.x);
+    const T* wp = static_cast<const T*>(p.w);
+
+    // DMA slots: thread-slot i*QNT + tid of a tile is chunk (row, pc) and
+    // holds logical chunk pc ^ swz(row) of that row (rows clamped to valid).
+    constexpr int DMA1 = QTILE / 16 / QNT;  // 4 loads per thread and tile
+    int64_t xoff[DMA1], woff[DMA1];
+#pragma unroll
+    for (int i = 0; i < DMA1; ++i) {
+        const int slot = i * QNT + tid;
+        const int row = slot / 8, pc = slot % 8;
+        const int xr = min(m0 + row, p.M - 1), wr = min(n0 + row, p.N - 1);
+        xoff[i] = (int64_t)xr * p.K + (pc ^ qswz(row)) * 8;
+        woff[i] = (int64_t)wr * p.K + (pc ^ qswz(row)) * 8;
+    }
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_q*)smem;
+    auto issue = [&](int kt) __attribute__((always_inline)) {
+        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + (kt % QNST) * QSTAGE + wave * 1024);
+        const int64_t k0 = (int64_t)kt * QBK;
+#pragma unroll
+        for (int i = 0; i < DMA1; ++i) {
+            qdma16(xp + xoff[i] + k0, st + i * QNT * 16);
+            qdma16(wp + woff[i] + k0, st + i * QNT * 16 + QTILE);
+        }
+    };
+    // operand of a 32-row block (rows rb*32.., K-step s) from a 128 x 64 tile
+    auto operand = [&](const unsigned char* tile, int rb, int s) __attribute__((always_inline)) -> u32x4 {
+        const int row = rb * 32 + n32;
+        const int lc = 2 * s + hh;
+        return *reinterpret_cast<const u32x4*>(tile + row * QROW + ((lc ^ qswz(row)) << 4));
+    };
+
+    f32x16 acc[2][2];  // [n block][m block] of Y^T
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b2][r] = 0.f;
+
+    const int nk = p.K / QBK;
+    issue(0);
+    for (int kt = 0; kt < nk; ++kt) {
+        qwait_vmcnt<0>();   // this thread's part of tile kt is in LDS
+        qbarrier();         // everyone's part; everyone is done with tile kt-1
+        if (kt + 1 < nk) issue(kt + 1);
+        const unsigned char* xt = smem + (kt % QNST) * QSTAGE;
+        const unsigned char* wt = xt + QTILE;
+#pragma unroll
+        for (int s = 0; s < QBK / 16; ++s) {
+            u32x4 wa[2], xb[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                wa[j] = operand(wt, wn * 2 + j, s);
+                xb[j] = operand(xt, wm * 2 + j, s);
+            }
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b2 = 0; b2 < 2; ++b2) acc[a][b2] = mfma16<Tag>(wa[a], xb[b2], acc[a][b2]);
+        }
+    }
+    __syncthreads();  // all DMA landed and all operand reads done
+
+    // ---- epilogue: Y tile (rows m, columns n) in LDS, then 16-byte stores ---
+    // acc[a][b2] register r of lane (n32, hh): column n = (wn*2+a)*32 +
+    // blk_row(r, hh) of the tile, row m = (wm*2+b2)*32 + n32.
+    T* Ys = reinterpret_cast<T*>(smem);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+            const int row = (wm * 2 + b2) * 32 + n32;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = (wn * 2 + a) * 32 + 8 * g + 4 * hh;
+                const f32x16& v = acc[a][b2];
+                const u32x2 pk = {pack2<Tag>(v[4 * g], v[4 * g + 1]), pack2<Tag>(v[4 * g + 2], v[4 * g + 3])};
+                *reinterpret_cast<u32x2*>(Ys + row * QOROW + col) = pk;
+            }
+        }
+    __syncthreads();
+    const int HD = p.H * p.d;
+    for (int cidx = tid; cidx < QBM * (QBN / 8); cidx += QNT) {
+        const int row = cidx / (QBN / 8), cc = cidx % (QBN / 8);
+        const int m = m0 + row, n = n0 + cc * 8;
+        if (m >= p.M || n >= p.N) continue;
+        const int t = n / HD, j = n - t * HD;
+        const int h = j / p.d, c = j - h * p.d;
+        const int b = m / p.S, s = m - b * p.S;
+        const int64_t dst = p.layout == 0 ? (((int64_t)b * p.H + h) * p.S + s) * p.d + c
+                                          : (int64_t)m * HD + j;
+        *reinterpret_cast<u32x4*>(static_cast<T*>(p.out[t]) + dst) =
+            *reinterpret_cast<const u32x4*>(Ys + row * QOROW + cc * 8);
+    }
+}
+
+}  // namespace
+
+hipError_t run_qkv_proj(const QkvArgs& a, hipStream_t stream) {
+    QkvParams p;
+    p.x = a.x;
+    p.w = a.w;
+    p.out[0] = a.q;
+    p.out[1] = a.k;
+    p.out[2] = a.v;
+    p.M = a.B * a.S;
+    p.N = 3 * a.H * a.d;
+    p.K = a.D;
+    p.S = a.S;
+    p.H = a.H;
+    p.d = a.d;
+    p.layout = a.layout;
+    p.n_ntiles = (p.N + QBN - 1) / QBN;
+    const int64_t grid = (int64_t)((p.M + QBM - 1) / QBM) * p.n_ntiles;
+    if (grid > 0x7fffffff || grid == 0) return grid == 0 ? hipSuccess : hipErrorInvalidValue;
+    if (a.dtype == 2)
+        hipLaunchKernelGGL(qkv_proj_kernel<BF16>, dim3((unsigned)grid), dim3(QNT), 0, stream, p);
+    else
+        hipLaunchKernelGGL(qkv_proj_kernel<F16>, dim3((unsigned)grid), dim3(QNT), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace attn

@@ -98,6 +98,17 @@ def generate(w: Workload, seed: int | None = None) -> dict:
     return out
 
 
+def generate_qkv_proj(B: int, S: int, D: int, H: int, d: int, dtype: str, seed: int) -> dict:
+    """Tokens x [B, S, D] ~ N(0, 1) and an out-major weight w [3*H*d, D] ~
+    N(0, 1/D) (a standard linear-layer initialisation: outputs of unit scale),
+    drawn in that order in float32 and cast to ``dtype`` (torch CPU tensors)."""
+    rng = np.random.default_rng(seed)
+    tdt = DTYPES[dtype]
+    x = rng.standard_normal((B, S, D), dtype=np.float32)
+    w = rng.standard_normal((3 * H * d, D), dtype=np.float32) * np.float32(1.0 / np.sqrt(D))
+    return {"x": torch.from_numpy(x).to(tdt), "w": torch.from_numpy(w).to(tdt)}
+
+
 def poison_padding(k: torch.Tensor, v: torch.Tensor, kv_len, layout: str) -> None:
     """Fill the key/value rows at or beyond each sequence's valid length with
     NaN, in place, so that any read of them shows up in the output."""

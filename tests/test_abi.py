@@ -131,6 +131,23 @@ def test_plan_and_size_queries(lib):
     assert lib.attn_naive_scratch_size(1, 1, 1, 1, 9) == 0
 
 
+def qkv(lib, x=A16, w=A16, q=A16_2, k=A16_2, v=A16_2, B=1, S=128, D=256, H=2, d=64,
+        layout=BHSD, dtype=BF16):
+    return lib.attn_qkv_proj(x, w, q, k, v, B, S, D, H, d, layout, dtype, None)
+
+
+def test_qkv_proj_validation(lib):
+    for bad in (dict(x=None), dict(w=None), dict(q=None), dict(k=None), dict(v=None)):
+        assert qkv(lib, **bad) == E_NULLPTR, bad
+    for bad in (dict(B=0), dict(S=0), dict(H=0), dict(D=0), dict(D=96), dict(D=32), dict(d=0),
+                dict(d=12), dict(B=1 << 16, S=1 << 16)):
+        assert qkv(lib, **bad) == E_SHAPE, bad
+    for bad in (dict(dtype=F32), dict(dtype=5), dict(layout=2)):
+        assert qkv(lib, **bad) == E_UNSUPPORTED, bad
+    for bad in (dict(x=A16 + 8), dict(w=A16 + 2), dict(q=A16_2 + 4), dict(v=A16_2 + 8)):
+        assert qkv(lib, **bad) == E_ALIGN, bad
+
+
 def test_python_binding_rejects_host_tensors(lib):
     q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
