@@ -15,7 +15,9 @@ its citations of the pages, is in that C file:
   Add an option to use online softmax instead of naive softmax", §四;
 * the (m, l) block merge: page "WebGPU 算子优化：QKV 内存合并与 FlashAttention
   分块计算", section "FlashAttention 分块计算原理与浏览器适配";
-* the QKV projection against the concatenated weight: the chapter's §2.1.
+* the QKV projection against the concatenated weight: the chapter's §2.1;
+* the softmax of rows on their own: the chapter's §2.3 steps, as the online
+  softmax page's §三-§四 treat it.
 
 Inputs are torch CPU tensors (float32, float16, bfloat16) or numpy arrays
 (float32, float16) in layout "bhsd" = [B, H, S, d] or "bshd" = [B, S, H, d].
@@ -66,6 +68,9 @@ class Oracle:
         lib.oracle_qkv_proj.argtypes = [_c_vp, _c_vp, _c_int, _c_int, _c_i64, _c_i64, _c_i64,
                                         _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_int]
         lib.oracle_qkv_proj.restype = _c_int
+        lib.oracle_softmax_rows.argtypes = [_c_vp, _c_int, _c_i64, _c_i64, _c_dbl, _c_vp, _c_vp,
+                                            _c_int]
+        lib.oracle_softmax_rows.restype = _c_int
         lib.oracle_decode.argtypes = [_c_vp, _c_i64, _c_int]
         lib.oracle_decode.restype = _c_dbl
         self.lib = lib
@@ -220,6 +225,20 @@ class Oracle:
         del xa, wa
         return tuple(outs)
 
+    def softmax_rows(self, x, *, scale=1.0, nthreads=None):
+        """Row softmax of x [rows, n] by definition. Returns (y [rows, n],
+        lse [rows]) as float64."""
+        rows, n = (int(a) for a in x.shape)
+        xa, xp, xc = self._buffer(x)
+        y = np.empty((rows, n), dtype=np.float64)
+        lse = np.empty((rows,), dtype=np.float64)
+        rc = self.lib.oracle_softmax_rows(xp, xc, rows, n, float(scale), y.ctypes.data,
+                                          lse.ctypes.data, self._threads(nthreads))
+        if rc:
+            raise RuntimeError(f"oracle_softmax_rows failed with code {rc}")
+        del xa
+        return y, lse
+
     def decode(self, x):
         """Every element of x decoded to float64 by the oracle's own reader."""
         keep, ptr, code = self._buffer(x)
@@ -267,3 +286,7 @@ def decode(*a, **kw):
 
 def qkv_proj(*a, **kw):
     return default().qkv_proj(*a, **kw)
+
+
+def softmax_rows(*a, **kw):
+    return default().softmax_rows(*a, **kw)

@@ -23,6 +23,8 @@
  *            (m, l) statistics of separate key blocks (test aid)
  *            section "QKV 矩阵的内存合并模式选择": Q, K, V of all heads, each
  *            in its own buffer of B x S x heads x d elements
+ *   [OSM]  §三-§四 softmax of a row of scores on its own (three passes,
+ *                or the one-pass online recurrence)
  *   [Ch2]  §2.1  the Q, K, V projections X W_Q, X W_K, X W_V, computed as one
  *                product with the three weight matrices side by side and
  *                then split
@@ -375,6 +377,44 @@ int oracle_qkv_proj(const void* x, const void* w, int dtype, int layout, int64_t
                         acc += load(x, bs * D + i, dtype) * load(w, n * D + i, dtype);
                     outs[t][at(layout, H, S, d, b, h, s_, c)] = acc;
                 }
+    }
+    return 0;
+}
+
+/*
+ * Row softmax by definition ([Ch2] §2.3 three steps, the computation [OSM]
+ * §三-§四 discusses on its own): for each row r of x [rows, n],
+ *   y[r, j] = exp(scale*x[r, j] - m_r) / l_r,  m_r = max_j scale*x[r, j],
+ *   l_r = sum_j exp(scale*x[r, j] - m_r),      lse[r] = m_r + ln l_r.
+ * Entries equal to -inf take no part (probability 0); a row with no finite
+ * entry gives y = 0 and lse = -inf. Outputs fp64. Returns 0, or 1 on bad
+ * sizes.
+ */
+int oracle_softmax_rows(const void* x, int dtype, int64_t rows, int64_t n, double scale,
+                        double* y, double* lse, int nthreads) {
+    if (rows < 0 || n < 1) return 1;
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t r = 0; r < rows; ++r) {
+        double m = -INFINITY;
+        for (int64_t j = 0; j < n; ++j) {                 /* step 1: the maximum */
+            const double v = load(x, r * n + j, dtype);
+            if (v == -INFINITY) continue;
+            if (scale * v > m) m = scale * v;
+        }
+        double* yr = y + r * n;
+        if (m == -INFINITY) {
+            for (int64_t j = 0; j < n; ++j) yr[j] = 0.0;
+            lse[r] = -INFINITY;
+            continue;
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < n; ++j) {                 /* step 2: the sum */
+            const double v = load(x, r * n + j, dtype);
+            yr[j] = v == -INFINITY ? 0.0 : exp(scale * v - m);
+            l += yr[j];
+        }
+        for (int64_t j = 0; j < n; ++j) yr[j] = yr[j] / l;   /* step 3: divide */
+        lse[r] = m + log(l);
     }
     return 0;
 }

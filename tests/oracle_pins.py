@@ -492,6 +492,53 @@ def pin_qkv_library(orc):
                 close(got[t], want[t], 1e-12, f"qkv vs einsum {layout} {dt} output {t}")
 
 
+
+def pin_softmax_rows_closed_forms(orc):
+    """Row softmax: the page's row [1.0, 2.0, 0.5, 3.0] against the 50-digit
+    closed form, rows summing to 1, the +1000 shift (a max-free softmax
+    overflows, this one may not), scale 0 giving uniform rows, -inf entries
+    taking no weight and an all -inf row giving 0 and lse = -inf."""
+    with open(os.path.join(GOLDEN, "online_softmax_row.json")) as f:
+        s = json.load(f)["scores"]
+    z = sum((_CTX.exp(D(x)) for x in s), D(0))
+    y, lse = orc.softmax_rows(np.array([s], dtype=np.float32))
+    close(y[0], [float(_CTX.exp(D(x)) / z) for x in s], 1e-15, "page row softmax")
+    close(lse[0], float(_CTX.ln(z)), 1e-15, "page row lse")
+    rng = np.random.default_rng(31)
+    # multiples of 2^-8, so that x + 1000 is exact in float32
+    x = (np.round(rand(rng, (6, 37)) * 3 * 256) / 256).astype(np.float32)
+    for sc in (1.0, 0.37):
+        y, lse = orc.softmax_rows(x, scale=sc)
+        close(y.sum(axis=1), np.ones(6), 1e-13, "row sums")
+        y2, lse2 = orc.softmax_rows(x + np.float32(1000.0), scale=sc)
+        close(y2, y, 1e-9, "shift by +1000")
+        close(lse2, lse + sc * 1000.0, 1e-9, "lse shift by +1000")
+    y, lse = orc.softmax_rows(x, scale=0.0)
+    close(y, np.full(x.shape, 1.0 / 37), 1e-15, "scale 0 is uniform")
+    close(lse, np.full(6, math.log(37)), 1e-13, "scale 0 lse")
+    xm = x.copy()
+    xm[0, 5:] = -np.inf
+    xm[1, :] = -np.inf
+    y, lse = orc.softmax_rows(xm)
+    close(y[0, 5:], np.zeros(32), 0.0, "-inf entries take no weight")
+    y0, _ = orc.softmax_rows(x[:1, :5].copy())
+    close(y[0, :5], y0[0], 1e-15, "-inf entries leave the rest unchanged")
+    close(y[1], np.zeros(37), 0.0, "all -inf row")
+    assert lse[1] == -np.inf, "all -inf row lse"
+
+
+def pin_softmax_rows_torch(orc):
+    """Library cross-check: torch.softmax / logsumexp in float64 on the
+    decoded inputs, all storage types."""
+    rng = np.random.default_rng(32)
+    for dt in (torch.float32, torch.float16, torch.bfloat16):
+        x = torch.from_numpy(rand(rng, (5, 129)) * 4).to(dt)
+        y, lse = orc.softmax_rows(x, scale=0.6)
+        xs = x.to(torch.float64) * 0.6
+        close(y, torch.softmax(xs, dim=1).numpy(), 1e-14, f"softmax vs torch {dt}")
+        close(lse, torch.logsumexp(xs, dim=1).numpy(), 1e-12, f"lse vs torch {dt}")
+
+
 ALL_PINS = [
     pin_decode_exact,
     pin_rows_sum_to_one,
@@ -509,4 +556,6 @@ ALL_PINS = [
     pin_rows_api,
     pin_qkv_identity,
     pin_qkv_library,
+    pin_softmax_rows_closed_forms,
+    pin_softmax_rows_torch,
 ]

@@ -40,6 +40,15 @@ MUTANTS = {
     "qkv heads interleaved": ("const int64_t n = t * HD + h * d + c;", "const int64_t n = t * HD + c * H + h;"),
     "qkv drops last input": ("for (int64_t i = 0; i < D; ++i)\n                        acc +=",
                              "for (int64_t i = 0; i + 1 < D; ++i)\n                        acc +="),
+    "softmax rows without max shift": ("yr[j] = v == -INFINITY ? 0.0 : exp(scale * v - m);",
+                                       "yr[j] = v == -INFINITY ? 0.0 : exp(scale * v);"),
+    "softmax rows scale dropped": ("yr[j] = v == -INFINITY ? 0.0 : exp(scale * v - m);",
+                                   "yr[j] = v == -INFINITY ? 0.0 : exp(v - m);"),
+    "softmax rows not normalised": ("for (int64_t j = 0; j < n; ++j) yr[j] = yr[j] / l;",
+                                    "for (int64_t j = 0; j < n; ++j) yr[j] = yr[j];"),
+    "softmax rows lse without max": ("lse[r] = m + log(l);", "lse[r] = log(l);"),
+    "softmax rows masked kept": ("yr[j] = v == -INFINITY ? 0.0 : exp(scale * v - m);",
+                                 "yr[j] = v == -INFINITY ? 1e-30 : exp(scale * v - m);"),
 }
 
 
