@@ -94,6 +94,49 @@ def cpu_baseline(w, t, target_s: float = 12.0):
                       f"{dt:.1f} s wall on {cores} threads (fp64, three-step softmax)"}
 
 
+def bench_softmax(args, w, torch, sdpa) -> int:
+    """Row softmax over score-like rows shaped like the workload's score
+    matrix: B*H*Sq rows of Sk, in the workload's dtype."""
+    from scaled_dot_product_flashattention_amd.inputs import generate_softmax_rows
+
+    rows, n = w.B * w.H * w.Sq, w.Sk
+    dev = torch.device("cuda:0")
+    x = generate_softmax_rows(rows, n, w.dtype, seed=w.seed).to(dev)
+    y = torch.empty_like(x)
+    lse = torch.empty((rows,), dtype=torch.float32, device=dev)
+    mode = args.path[len("softmax_"):]
+    step = lambda: sdpa.attn_softmax_rows(x, scale=w.scale, mode=mode, out=y, lse=lse)  # noqa: E731
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    es = x.element_size()
+    nbytes = float(rows) * n * 2 * es + rows * 4  # x read once, y written once, lse
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": f"row softmax ({mode}) GB/s, {rows} rows of {n} ({w.name} score rows)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": {"f32": "f32", "f16": "fp16", "bf16": "bf16"}[w.dtype], "data": "synthetic",
+        "config": {"workload": w.name, "rows": rows, "n": n, "path": args.path},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel_ms": round(ms, 5),
+                     "algorithmic_units": "bytes per launch (x once, y once, lse)",
+                     "algorithmic_per_launch": nbytes},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_qkv(args, w, torch, sdpa) -> int:
     """QKV projection of the workload's tokens (model width D = H*d, the
     weight [3*H*d, D]), alone or followed by the attention of the workload."""
@@ -168,11 +211,13 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--config", default="medium_bf16")
     ap.add_argument("--path", default="fused",
-                    choices=["fused", "naive", "splitk", "qkv", "qkv_attn", "qkv_attn_unfused"],
+                    choices=["fused", "naive", "splitk", "qkv", "qkv_attn", "qkv_attn_unfused",
+                             "softmax_online", "softmax_three_pass"],
                     help="fused attention (default), the unfused baseline, the explicit "
                          "split-K path, the QKV projection alone, projection + attention, "
-                         "or the unfused sequence (three library matmuls and layout "
-                         "copies, then attention)")
+                         "the unfused sequence (three library matmuls and layout "
+                         "copies, then attention), or the row softmax (online or "
+                         "three-pass) over the workload's B*H*Sq score rows of Sk")
     ap.add_argument("--n-split", type=int, default=None)
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -197,6 +242,8 @@ def main() -> int:
     w = WORKLOADS[args.config]
     if args.path.startswith("qkv"):
         return bench_qkv(args, w, torch, sdpa)
+    if args.path.startswith("softmax"):
+        return bench_softmax(args, w, torch, sdpa)
     t = generate(w)
     dev = torch.device("cuda:0")
     q, k, v = (t[n].to(dev) for n in ("q", "k", "v"))

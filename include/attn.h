@@ -146,6 +146,34 @@ size_t attn_naive_scratch_size(int B, int H, int Sq, int Sk, int dtype);
 int attn_qkv_proj(const void* x, const void* w, void* q, void* k, void* v, int B, int S, int D,
                   int H, int d, int layout, int dtype, void* stream);
 
+/*
+ * Row softmax: for each row r of x [rows, n],
+ *     y[r, j] = exp(scale*x[r, j] - m_r) / l_r,   lse[r] = m_r + ln l_r,
+ * with m_r the row maximum of scale*x and l_r the sum of the shifted
+ * exponentials (§2.3 of the chapter). Entries equal to -inf get probability 0;
+ * a row with no finite entry gives y = 0 and lse = -inf. This is the
+ * computation the page "[Performance] [WebGPU] Proposal: Add an option to use
+ * online softmax instead of naive softmax" studies on its own, in its two
+ * forms, selected by `mode`:
+ *   ATTN_SOFTMAX_ONLINE     the online form: a running max and a running sum
+ *                           rescaled as the max grows (§四 of that page). Rows
+ *                           of up to 32768 elements are read from memory once
+ *                           (held on chip); longer rows twice.
+ *   ATTN_SOFTMAX_THREE_PASS the naive form: separate passes for the max, the
+ *                           sum and the normalisation, each reading the row.
+ * Storage: x and y dense [rows, n] of `dtype` (any of the three), y may not
+ * alias x; lse float32 [rows] or NULL. n must be a multiple of 8 for 16-bit
+ * types and of 4 for fp32 (16-byte rows); 1 <= rows < 2^31 (ATTN_E_SHAPE);
+ * scale finite and >= 0 (ATTN_E_ARG; 0 gives uniform rows over the finite
+ * entries); x, y 16-byte and lse 4-byte aligned (ATTN_E_ALIGN). fp32
+ * arithmetic, base-2 exponentials; y is rounded once to `dtype`.
+ * Asynchronous on `stream` like attn_fwd; no workspace.
+ */
+enum attn_softmax_mode { ATTN_SOFTMAX_ONLINE = 0, ATTN_SOFTMAX_THREE_PASS = 1 };
+
+int attn_softmax_rows(const void* x, void* y, float* lse, int64_t rows, int n, float scale,
+                      int dtype, int mode, void* stream);
+
 /* Static text for a status code. */
 const char* attn_status_string(int status);
 

@@ -58,6 +58,8 @@ def load_library() -> ctypes.CDLL:
     L.attn_naive_scratch_size.restype = sz
     L.attn_qkv_proj.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     L.attn_qkv_proj.restype = i
+    L.attn_softmax_rows.argtypes = [vp, vp, vp, ctypes.c_int64, i, f, i, i, vp]
+    L.attn_softmax_rows.restype = i
     L.attn_status_string.argtypes = [i]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_version.argtypes = []
@@ -237,3 +239,29 @@ def attn_qkv_proj(x, w, *, H, d, layout="bhsd", out=None, stream=None):
     if rc:
         raise AttnError("attn_qkv_proj", rc)
     return tuple(out)
+
+
+_SOFTMAX_MODES = {"online": 0, "three_pass": 1}
+
+
+def attn_softmax_rows(x, *, scale=1.0, mode="online", return_lse=True, out=None, lse=None,
+                      stream=None):
+    """Row softmax of x [rows, n] (2-D, contiguous, on the GPU). mode is
+    "online" or "three_pass". Returns (y, lse); lse is None when return_lse
+    is False."""
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.dim() != 2:
+        raise ValueError("x must be a 2-D CUDA (HIP) tensor")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    rows, n = (int(a) for a in x.shape)
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
+        raise ValueError("out must match x in shape and dtype")
+    if lse is None and return_lse:
+        lse = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    rc = load_library().attn_softmax_rows(_ptr(x), _ptr(y), _ptr(lse), rows, n, float(scale),
+                                          dtype_code(x.dtype), _SOFTMAX_MODES[mode],
+                                          _stream(x, stream))
+    if rc:
+        raise AttnError("attn_softmax_rows", rc)
+    return y, lse

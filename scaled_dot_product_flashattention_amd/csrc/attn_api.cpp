@@ -176,6 +176,27 @@ int attn_qkv_proj(const void* x, const void* w, void* q, void* k, void* v, int B
     return status_of(attn::run_qkv_proj(a, static_cast<hipStream_t>(stream)));
 }
 
+int attn_softmax_rows(const void* x, void* y, float* lse, int64_t rows, int n, float scale,
+                      int dtype, int mode, void* stream) {
+    if (!x || !y) return ATTN_E_NULLPTR;
+    if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
+    if (mode != ATTN_SOFTMAX_ONLINE && mode != ATTN_SOFTMAX_THREE_PASS) return ATTN_E_UNSUPPORTED;
+    const int per16 = dtype == ATTN_F32 ? 4 : 8;  // elements per 16 bytes
+    if (rows < 1 || rows > INT_MAX || n < 1 || n % per16 != 0) return ATTN_E_SHAPE;
+    if (!std::isfinite(scale) || scale < 0.f) return ATTN_E_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(lse, 4)) return ATTN_E_ALIGN;
+    attn::SoftmaxArgs a;
+    a.x = x;
+    a.y = y;
+    a.lse = lse;
+    a.rows = rows;
+    a.n = n;
+    a.scale = scale;
+    a.dtype = dtype;
+    a.mode = mode;
+    return status_of(attn::run_softmax_rows(a, static_cast<hipStream_t>(stream)));
+}
+
 const char* attn_status_string(int status) {
     switch (status) {
     case ATTN_OK: return "ok";

@@ -43,6 +43,19 @@ struct QkvArgs {
 };
 hipError_t run_qkv_proj(const QkvArgs& a, hipStream_t stream);
 
+// Row softmax of x [rows, n] (mode 0 online, 1 three-pass).
+struct SoftmaxArgs {
+    const void* x;
+    void* y;
+    float* lse;
+    int64_t rows;
+    int n;
+    float scale;
+    int dtype;
+    int mode;
+};
+hipError_t run_softmax_rows(const SoftmaxArgs& a, hipStream_t stream);
+
 // Unfused three-kernel baseline.
 size_t naive_scratch_bytes(int B, int H, int Sq, int Sk, int dtype);
 hipError_t run_naive(const FwdArgs& a, void* scratch, hipStream_t stream);

@@ -109,6 +109,14 @@ def generate_qkv_proj(B: int, S: int, D: int, H: int, d: int, dtype: str, seed: 
     return {"x": torch.from_numpy(x).to(tdt), "w": torch.from_numpy(w).to(tdt)}
 
 
+def generate_softmax_rows(rows: int, n: int, dtype: str, seed: int, std: float = 2.0) -> torch.Tensor:
+    """Score-like rows x [rows, n] ~ N(0, std^2) in float32, cast to ``dtype``
+    (torch CPU tensor)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, n), dtype=np.float32) * np.float32(std)
+    return torch.from_numpy(x).to(DTYPES[dtype])
+
+
 def poison_padding(k: torch.Tensor, v: torch.Tensor, kv_len, layout: str) -> None:
     """Fill the key/value rows at or beyond each sequence's valid length with
     NaN, in place, so that any read of them shows up in the output."""

@@ -148,6 +148,23 @@ def test_qkv_proj_validation(lib):
         assert qkv(lib, **bad) == E_ALIGN, bad
 
 
+def smx(lib, x=A16, y=A16_2, lse=None, rows=4, n=64, scale=1.0, dtype=BF16, mode=0):
+    return lib.attn_softmax_rows(x, y, lse, rows, n, scale, dtype, mode, None)
+
+
+def test_softmax_rows_validation(lib):
+    assert smx(lib, x=None) == E_NULLPTR and smx(lib, y=None) == E_NULLPTR
+    for bad in (dict(rows=0), dict(rows=-1), dict(rows=1 << 31), dict(n=0), dict(n=12),
+                dict(n=6, dtype=F32)):
+        assert smx(lib, **bad) == E_SHAPE, bad
+    for bad in (dict(dtype=3), dict(mode=2), dict(mode=-1)):
+        assert smx(lib, **bad) == E_UNSUPPORTED, bad
+    for bad in (float("nan"), float("inf"), -1.0):
+        assert smx(lib, scale=bad) == E_ARG, bad
+    for bad in (dict(x=A16 + 8), dict(y=A16_2 + 4), dict(lse=A16 + 2)):
+        assert smx(lib, **bad) == E_ALIGN, bad
+
+
 def test_python_binding_rejects_host_tensors(lib):
     q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
