@@ -147,7 +147,10 @@ def bench_qkv(args, w, torch, sdpa) -> int:
     dev = torch.device("cuda:0")
     t = generate_qkv_proj(B, S, D, H, d, w.dtype, seed=w.seed)
     x, wt = t["x"].to(dev), t["w"].to(dev)
-    shape = (B, H, S, d) if w.layout == "bhsd" else (B, S, H, d)
+    shape = sdpa.api.layout_shape(w.layout, B, H, S, d)
+    if args.path == "qkv_attn_unfused" and w.layout not in ("bhsd", "bshd"):
+        print("the unfused sequence is written for [B,H,S,d] and [B,S,H,d] only", file=sys.stderr)
+        return 2
     qkv = tuple(torch.empty(shape, dtype=x.dtype, device=dev) for _ in range(3))
     o = torch.empty(shape, dtype=x.dtype, device=dev)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
@@ -219,6 +222,9 @@ def main() -> int:
                          "copies, then attention), or the row softmax (online or "
                          "three-pass) over the workload's B*H*Sq score rows of Sk")
     ap.add_argument("--n-split", type=int, default=None)
+    ap.add_argument("--layout", default=None,
+                    help="override the workload's tensor layout: bhsd ([B,H,S,d]), bshd "
+                         "([B,S,H,d]) or split:g ([B,H/g,S,g,d], heads in groups of g)")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run 3 plain device copies of 256 MiB so a "
@@ -240,6 +246,9 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     w = WORKLOADS[args.config]
+    relaid = args.layout is not None and args.layout != w.layout
+    if relaid:
+        w = w.replace(layout=args.layout)
     if args.path.startswith("qkv"):
         return bench_qkv(args, w, torch, sdpa)
     if args.path.startswith("softmax"):
@@ -304,13 +313,13 @@ def main() -> int:
         peak = PEAK_TFLOPS_F32 if w.dtype == "f32" else PEAK_TFLOPS_16
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(tflops / peak, 4)}
-        if args.config == "medium_bf16" and args.path == "fused":
+        if args.config == "medium_bf16" and args.path == "fused" and not relaid:
             metric = "fused attention fwd TFLOP/s and % bf16 MFMA peak, B1 H16 S4096 d64"
         else:
             metric = f"attention fwd TFLOP/s ({args.path}), {w.description}"
         value, unit = tflops, "TFLOP/s"
     kind = "splitk" if decode else args.path
-    roof["traffic"] = stored_traffic(args.config, args.path, kind)
+    roof["traffic"] = None if relaid else stored_traffic(args.config, args.path, kind)
     roof["kernel_ms"] = round(ms, 5)
     roof["algorithmic_units"] = ("bytes of K and V per launch" if decode else "FLOPs per launch")
     roof["algorithmic_per_launch"] = kv_bytes(w) if decode else fl

@@ -29,7 +29,8 @@
  *   kv_len int32 [B] or NULL.
  * The two layouts are the "Contiguous" and head-"Interleaved" QKV layouts of
  * the section "QKV 矩阵的内存合并模式选择" of the WebGPU page, read as
- * separate q, k, v tensors with heads outermost or interleaved per token.
+ * separate q, k, v tensors with heads outermost or interleaved per token;
+ * its "Split" layout is ATTN_LAYOUT_SPLIT(g) below.
  * q, k, v, o and workspaces must be 16-byte aligned; lse and kv_len 4-byte.
  *
  * Arithmetic: bf16/fp16 inputs use bf16/fp16 matrix-core products with fp32
@@ -59,7 +60,7 @@ enum attn_status {
     ATTN_OK = 0,
     ATTN_E_NULLPTR = 1,     /* a required pointer is NULL                        */
     ATTN_E_SHAPE = 2,       /* B, H, Sq or Sk < 1, n_split < 1, or sizes overflow */
-    ATTN_E_UNSUPPORTED = 3, /* d not 64 or 128, or an enum value out of range    */
+    ATTN_E_UNSUPPORTED = 3, /* d not 64/128, enum out of range, group not dividing H */
     ATTN_E_ALIGN = 4,       /* a pointer is not aligned as stated above          */
     ATTN_E_WORKSPACE = 5,   /* workspace / scratch NULL or smaller than required */
     ATTN_E_HIP = 6,         /* the HIP runtime reported an error at launch       */
@@ -67,6 +68,12 @@ enum attn_status {
 };
 
 enum attn_layout { ATTN_LAYOUT_BHSD = 0, ATTN_LAYOUT_BSHD = 1 };
+
+/* The "Split" head-group layout of the same section: heads in groups of g,
+ * each group's rows stored together, [B, H/g, S, g, d]. g must divide H.
+ * g = 1 is the same memory order as ATTN_LAYOUT_BHSD, g = H as
+ * ATTN_LAYOUT_BSHD. Accepted wherever a layout is. */
+#define ATTN_LAYOUT_SPLIT(g) (0x10000 | (g))
 
 enum attn_dtype { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 };
 
@@ -134,8 +141,9 @@ size_t attn_naive_scratch_size(int B, int H, int Sq, int Sk, int dtype);
  *   x      [B, S, D] dense, element type `dtype`.
  *   w      [3*H*d, D] dense: w[n*D + i] = W[i, n] (out-major, the storage of
  *          a linear layer's weight), element type `dtype`.
- *   q,k,v  [B, H, S, d] (ATTN_LAYOUT_BHSD) or [B, S, H, d] (ATTN_LAYOUT_BSHD),
- *          dense, element type `dtype`: the inputs attn_fwd takes.
+ *   q,k,v  [B, H, S, d] (ATTN_LAYOUT_BHSD), [B, S, H, d] (ATTN_LAYOUT_BSHD) or
+ *          [B, H/g, S, g, d] (ATTN_LAYOUT_SPLIT(g)), dense, element type
+ *          `dtype`: the inputs attn_fwd takes.
  * dtype is ATTN_F16 or ATTN_BF16 (fp32 returns ATTN_E_UNSUPPORTED); products
  * accumulate in fp32 and each output is rounded once (nearest-even).
  * Requirements: B, S >= 1 (else ATTN_E_SHAPE); D a positive multiple of 64

@@ -20,7 +20,8 @@ its citations of the pages, is in that C file:
   softmax page's §三-§四 treat it.
 
 Inputs are torch CPU tensors (float32, float16, bfloat16) or numpy arrays
-(float32, float16) in layout "bhsd" = [B, H, S, d] or "bshd" = [B, S, H, d].
+(float32, float16) in layout "bhsd" = [B, H, S, d], "bshd" = [B, S, H, d] or
+"split:g" = [B, H/g, S, g, d].
 Outputs are float64 numpy arrays: O in the layout of q, LSE as [B, H, Sq].
 """
 from __future__ import annotations
@@ -35,6 +36,24 @@ from .build import build as _build, library_path
 
 _DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 _LAYOUT_CODES = {"bhsd": 0, "bshd": 1}
+
+
+def layout_code(layout: str) -> int:
+    """"bhsd" = [B,H,S,d], "bshd" = [B,S,H,d], "split:g" = [B,H/g,S,g,d]."""
+    if layout in _LAYOUT_CODES:
+        return _LAYOUT_CODES[layout]
+    if layout.startswith("split:"):
+        return 0x10000 | int(layout[6:])
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def layout_shape(layout: str, B: int, H: int, S: int, d: int) -> tuple:
+    if layout == "bhsd":
+        return (B, H, S, d)
+    if layout == "bshd":
+        return (B, S, H, d)
+    g = layout_code(layout) & 0xffff
+    return (B, H // g, S, g, d)
 
 _c_i64 = ctypes.c_int64
 _c_int = ctypes.c_int
@@ -105,6 +124,9 @@ class Oracle:
         elif layout == "bshd":
             B, Sq, H, d = q.shape
             Sk = k.shape[1]
+        elif layout.startswith("split:"):
+            B, G, Sq, g, d = q.shape
+            H, Sk = G * g, k.shape[2]
         else:
             raise ValueError(f"unknown layout {layout!r}")
         return int(B), int(H), int(Sq), int(Sk), int(d)
@@ -134,7 +156,7 @@ class Oracle:
                 raise ValueError("kv_len must have shape [B]")
             keep.append(la)
             lp = la.ctypes.data
-        args = [qp, kp, vp, qc, _LAYOUT_CODES[layout], B, H, Sq, Sk, d, float(scale),
+        args = [qp, kp, vp, qc, layout_code(layout), B, H, Sq, Sk, d, float(scale),
                 int(bool(causal)), lp]
         return keep, args, (B, H, Sq, Sk, d)
 
@@ -216,9 +238,9 @@ class Oracle:
         wa, wp, wc = self._buffer(w)
         if xc != wc:
             raise TypeError("x and w must share one dtype")
-        shape = (B, H, S, d) if layout == "bhsd" else (B, S, H, d)
+        shape = layout_shape(layout, B, H, S, d)
         outs = [np.empty(shape, dtype=np.float64) for _ in range(3)]
-        rc = self.lib.oracle_qkv_proj(xp, wp, xc, _LAYOUT_CODES[layout], B, S, D, H, d,
+        rc = self.lib.oracle_qkv_proj(xp, wp, xc, layout_code(layout), B, S, D, H, d,
                                       *(o.ctypes.data for o in outs), self._threads(nthreads))
         if rc:
             raise RuntimeError(f"oracle_qkv_proj failed with code {rc}")

@@ -22,7 +22,9 @@
  *            section "FlashAttention 分块计算原理与浏览器适配": merging the
  *            (m, l) statistics of separate key blocks (test aid)
  *            section "QKV 矩阵的内存合并模式选择": Q, K, V of all heads, each
- *            in its own buffer of B x S x heads x d elements
+ *            in its own buffer of B x S x heads x d elements, heads outermost
+ *            ("Contiguous"), interleaved per token ("Interleaved") or in
+ *            groups of heads stored together ("Split")
  *   [OSM]  §三-§四 softmax of a row of scores on its own (three passes,
  *                or the one-pass online recurrence)
  *   [Ch2]  §2.1  the Q, K, V projections X W_Q, X W_K, X W_V, computed as one
@@ -56,6 +58,7 @@
 /* layouts, oracle-side codes */
 #define ORC_BHSD 0 /* [B, H, S, d]: all rows of one head contiguous      */
 #define ORC_BSHD 1 /* [B, S, H, d]: heads interleaved within each token  */
+#define ORC_SPLIT 0x10000 /* | g: [B, H/g, S, g, d], groups of g heads    */
 
 /* ---- exact decoding of one stored element to double -------------------- */
 
@@ -98,7 +101,18 @@ double oracle_decode(const void* base, int64_t idx, int dtype) {
 static int64_t at(int layout, int64_t H, int64_t S, int64_t d,
                   int64_t b, int64_t h, int64_t s, int64_t c) {
     if (layout == ORC_BHSD) return ((b * H + h) * S + s) * d + c;
-    return ((b * S + s) * H + h) * d + c;
+    if (layout == ORC_BSHD) return ((b * S + s) * H + h) * d + c;
+    /* [Blog] "Split": heads in groups of g, [B, H/g, S, g, d] */
+    const int64_t g = layout & 0xffff;
+    return (((b * (H / g) + h / g) * S + s) * g + h % g) * d + c;
+}
+
+/* a layout code the oracle knows: BHSD, BSHD, or ORC_SPLIT | g with g | H */
+static int layout_valid(int layout, int64_t H) {
+    if (layout == ORC_BHSD || layout == ORC_BSHD) return 1;
+    if ((layout & ~0xffff) != ORC_SPLIT) return 0;
+    const int64_t g = layout & 0xffff;
+    return g >= 1 && H % g == 0;
 }
 
 typedef struct {
@@ -186,7 +200,7 @@ static int check(const problem* p) {
     if (!p->q || !p->k || !p->v) return 1;
     if (p->B < 1 || p->H < 1 || p->Sq < 1 || p->Sk < 1 || p->d < 1) return 2;
     if (p->dtype < ORC_F32 || p->dtype > ORC_BF16) return 3;
-    if (p->layout != ORC_BHSD && p->layout != ORC_BSHD) return 3;
+    if (!layout_valid(p->layout, p->H)) return 3;
     return 0;
 }
 
@@ -361,7 +375,7 @@ int oracle_qkv_proj(const void* x, const void* w, int dtype, int layout, int64_t
                     int64_t D, int64_t H, int64_t d, double* q, double* k, double* v,
                     int nthreads) {
     if (B < 0 || S < 0 || D < 1 || H < 1 || d < 1) return 1;
-    if (layout != ORC_BHSD && layout != ORC_BSHD) return 1;
+    if (!layout_valid(layout, H)) return 1;
     double* outs[3] = {q, k, v};
     const int64_t HD = H * d;
     (void)nthreads;

@@ -19,6 +19,25 @@ _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _LAYOUT = {"bhsd": 0, "bshd": 1}
 
 
+def layout_code(layout: str) -> int:
+    """"bhsd" = [B,H,S,d], "bshd" = [B,S,H,d], "split:g" = [B,H/g,S,g,d]
+    (ATTN_LAYOUT_SPLIT(g): heads in groups of g)."""
+    if layout in _LAYOUT:
+        return _LAYOUT[layout]
+    if isinstance(layout, str) and layout.startswith("split:"):
+        return 0x10000 | int(layout[6:])
+    raise ValueError(f"layout must be 'bhsd', 'bshd' or 'split:g', not {layout!r}")
+
+
+def layout_shape(layout: str, B: int, H: int, S: int, d: int) -> tuple:
+    if layout == "bhsd":
+        return (B, H, S, d)
+    if layout == "bshd":
+        return (B, S, H, d)
+    g = layout_code(layout) & 0xffff
+    return (B, H // g, S, g, d)
+
+
 class AttnError(RuntimeError):
     """A libattn call returned a nonzero status."""
 
@@ -111,8 +130,13 @@ def dims(q: torch.Tensor, k: torch.Tensor, layout: str):
     elif layout == "bshd":
         B, Sq, H, d = q.shape
         Sk = k.shape[1]
+    elif isinstance(layout, str) and layout.startswith("split:"):
+        B, G, Sq, g, d = q.shape
+        H, Sk = G * g, k.shape[2]
+        if g != (layout_code(layout) & 0xffff):
+            raise ValueError(f"q has groups of {g} heads, layout says {layout!r}")
     else:
-        raise ValueError(f"layout must be 'bhsd' or 'bshd', not {layout!r}")
+        raise ValueError(f"layout must be 'bhsd', 'bshd' or 'split:g', not {layout!r}")
     return int(B), int(H), int(Sq), int(Sk), int(d)
 
 
@@ -124,10 +148,10 @@ def _prepare(q, k, v, layout, kv_len, scale, lse, return_lse, out):
             raise ValueError(f"{name} must be contiguous in the {layout} layout")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share one dtype")
-    if q.dim() != 4 or k.dim() != 4 or tuple(k.shape) != tuple(v.shape):
-        raise ValueError("q, k, v must be 4-D and k, v must have the same shape")
+    if q.dim() != k.dim() or tuple(k.shape) != tuple(v.shape):
+        raise ValueError("q, k, v must have the same rank and k, v the same shape")
     B, H, Sq, Sk, d = dims(q, k, layout)
-    kshape = (B, H, Sk, d) if layout == "bhsd" else (B, Sk, H, d)
+    kshape = layout_shape(layout, B, H, Sk, d)
     if tuple(k.shape) != kshape:
         raise ValueError(f"k has shape {tuple(k.shape)}, expected {kshape}")
     if kv_len is not None:
@@ -171,7 +195,7 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, layout="bhsd", kv_len=None, r
     nbytes = attn_fwd_workspace_size(B, H, Sq, Sk, d, q.dtype)
     ws = _scratch(nbytes, q.device, workspace)
     rc = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq, Sk, d,
-                                 scale, int(bool(causal)), _LAYOUT[layout], dt, _ptr(kv_len),
+                                 scale, int(bool(causal)), layout_code(layout), dt, _ptr(kv_len),
                                  _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                  _stream(q, stream))
     if rc:
@@ -187,7 +211,7 @@ def attn_fwd_splitk(q, k, v, *, n_split, scale=None, causal=False, layout="bhsd"
     nbytes = attn_splitk_workspace_size(B, H, Sq, d, int(n_split))
     ws = _scratch(nbytes, q.device, workspace)
     rc = load_library().attn_fwd_splitk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq,
-                                        Sk, d, scale, int(bool(causal)), _LAYOUT[layout],
+                                        Sk, d, scale, int(bool(causal)), layout_code(layout),
                                         dtype_code(q.dtype), _ptr(kv_len), int(n_split), _ptr(ws),
                                         0 if ws is None else ws.numel() * ws.element_size(),
                                         _stream(q, stream))
@@ -204,7 +228,7 @@ def attn_fwd_naive(q, k, v, *, scale=None, causal=False, layout="bhsd", kv_len=N
     nbytes = attn_naive_scratch_size(B, H, Sq, Sk, q.dtype)
     sc = _scratch(nbytes, q.device, scratch)
     rc = load_library().attn_fwd_naive(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq,
-                                       Sk, d, scale, int(bool(causal)), _LAYOUT[layout],
+                                       Sk, d, scale, int(bool(causal)), layout_code(layout),
                                        dtype_code(q.dtype), _ptr(kv_len), _ptr(sc),
                                        0 if sc is None else sc.numel() * sc.element_size(),
                                        _stream(q, stream))
@@ -227,14 +251,14 @@ def attn_qkv_proj(x, w, *, H, d, layout="bhsd", out=None, stream=None):
     B, S, D = (int(n) for n in x.shape)
     if tuple(w.shape) != (3 * H * d, D):
         raise ValueError(f"w has shape {tuple(w.shape)}, expected {(3 * H * d, D)}")
-    shape = (B, H, S, d) if layout == "bhsd" else (B, S, H, d)
+    shape = layout_shape(layout, B, int(H), S, int(d))
     if out is None:
         out = tuple(torch.empty(shape, dtype=x.dtype, device=x.device) for _ in range(3))
     for t in out:
         if tuple(t.shape) != shape or t.dtype != x.dtype or not t.is_contiguous():
             raise ValueError("out tensors must be dense, of x's dtype and shape " + str(shape))
     rc = load_library().attn_qkv_proj(_ptr(x), _ptr(w), *(_ptr(t) for t in out), B, S, D, int(H),
-                                      int(d), _LAYOUT[layout], dtype_code(x.dtype),
+                                      int(d), layout_code(layout), dtype_code(x.dtype),
                                       _stream(x, stream))
     if rc:
         raise AttnError("attn_qkv_proj", rc)

@@ -22,10 +22,18 @@ constexpr int kSplitMinKeys = 512;      // keys per split, at least
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// [B,H,S,d], [B,S,H,d], or groups of g heads (1 <= g, g divides H)
+bool layout_ok(int layout, int H) {
+    if (layout == ATTN_LAYOUT_BHSD || layout == ATTN_LAYOUT_BSHD) return true;
+    if ((layout & ~0xffff) != ATTN_LAYOUT_SPLIT(0)) return false;
+    const int g = layout & 0xffff;
+    return g >= 1 && H % g == 0;
+}
+
 int check_shape(int B, int H, int Sq, int Sk, int d, int layout, int dtype) {
     if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return ATTN_E_SHAPE;
     if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
-    if (layout != ATTN_LAYOUT_BHSD && layout != ATTN_LAYOUT_BSHD) return ATTN_E_UNSUPPORTED;
+    if (!layout_ok(layout, H)) return ATTN_E_UNSUPPORTED;
     if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
     // every row index (b*H + h)*S + s and every workgroup count fits in int32
     const int64_t rows_q = (int64_t)B * H * Sq;
@@ -154,7 +162,8 @@ int attn_fwd_naive(const void* q, const void* k, const void* v, void* o, float* 
 int attn_qkv_proj(const void* x, const void* w, void* q, void* k, void* v, int B, int S, int D,
                   int H, int d, int layout, int dtype, void* stream) {
     if (!x || !w || !q || !k || !v) return ATTN_E_NULLPTR;
-    if (layout != ATTN_LAYOUT_BHSD && layout != ATTN_LAYOUT_BSHD) return ATTN_E_UNSUPPORTED;
+    if (H < 1) return ATTN_E_SHAPE;
+    if (!layout_ok(layout, H)) return ATTN_E_UNSUPPORTED;
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
     if (B < 1 || S < 1 || H < 1 || D < 64 || D % 64 != 0 || d < 8 || d % 8 != 0) return ATTN_E_SHAPE;
     if ((int64_t)B * S > INT_MAX || (int64_t)3 * H * d > INT_MAX) return ATTN_E_SHAPE;

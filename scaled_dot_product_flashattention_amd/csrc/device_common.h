@@ -102,16 +102,38 @@ __device__ __forceinline__ float swap_halves(float x) {
 __device__ __forceinline__ constexpr int blk_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
 // ---- addressing -------------------------------------------------------------
-// Strides in elements of one tensor, for either layout.
+// Element offsets in one tensor of B x H heads x S rows x d, for the three
+// layouts: heads in groups of g, [B, H/g, S, g, d]. g = 1 is [B,H,S,d]
+// (heads outermost), g = H is [B,S,H,d] (heads interleaved per token), and
+// anything between is the "Split" head-group layout.
 struct Strides {
-    int64_t b;  // between batches
-    int64_t h;  // between heads
-    int64_t s;  // between consecutive rows (tokens) of one head
+    int64_t b;    // between batches
+    int64_t grp;  // between head groups
+    int64_t s;    // between consecutive rows (tokens) of one head
+    int hd;       // between heads of one group
+    int g;        // heads per group
+    __host__ __device__ int64_t head(int bi, int h) const {
+        return bi * b + (int64_t)(h / g) * grp + (int64_t)(h % g) * hd;
+    }
 };
 
+// Layout codes (see include/attn.h): 0 = [B,H,S,d], 1 = [B,S,H,d],
+// 0x10000 | g = groups of g heads. Returns the heads per group.
+__host__ __device__ inline int layout_group(int layout, int H) {
+    if (layout == 0) return 1;
+    if (layout == 1) return H;
+    return layout & 0xffff;
+}
+
 __host__ __device__ inline Strides make_strides(int layout, int H, int S, int d) {
-    if (layout == 0) return Strides{(int64_t)H * S * d, (int64_t)S * d, (int64_t)d};  // [B,H,S,d]
-    return Strides{(int64_t)S * H * d, (int64_t)d, (int64_t)H * d};                   // [B,S,H,d]
+    const int g = layout_group(layout, H);
+    Strides st;
+    st.b = (int64_t)S * H * d;
+    st.grp = (int64_t)S * g * d;
+    st.s = (int64_t)g * d;
+    st.hd = d;
+    st.g = g;
+    return st;
 }
 
 // Transposed LDS store of two consecutive 16-bit key rows (keys 2*pr and

@@ -176,10 +176,10 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
     const int kend = p.causal ? min(nb, q_end) : nb;  // keys any row of the tile can see
     const int ntiles = (kend + BN - 1) / BN;
 
-    const T* qp = static_cast<const T*>(p.q) + b * p.sq.b + h * p.sq.h;
-    const T* kp = static_cast<const T*>(p.k) + b * p.sk.b + h * p.sk.h;
-    const T* vp = static_cast<const T*>(p.v) + b * p.sk.b + h * p.sk.h;
-    T* op = static_cast<T*>(p.o) + b * p.sq.b + h * p.sq.h;
+    const T* qp = static_cast<const T*>(p.q) + p.sq.head(b, h);
+    const T* kp = static_cast<const T*>(p.k) + p.sk.head(b, h);
+    const T* vp = static_cast<const T*>(p.v) + p.sk.head(b, h);
+    T* op = static_cast<T*>(p.o) + p.sq.head(b, h);
 
     const int qw0 = q0 + wq * 32 * NQ;  // first query row of this wave
     // Waves past the last query row compute on zero queries and store nothing.

@@ -94,9 +94,9 @@ __global__ __launch_bounds__(256) void splitk_partial_kernel(SplitParams p) {
     const int ks = split * p.chunk;
     const int ke = min(ks + p.chunk, lim);
 
-    const T* qrow = static_cast<const T*>(p.q) + b * p.sq.b + h * p.sq.h + (int64_t)i * p.sq.s;
-    const T* kb = static_cast<const T*>(p.k) + b * p.sk.b + h * p.sk.h + sub * EPL;
-    const T* vb = static_cast<const T*>(p.v) + b * p.sk.b + h * p.sk.h + sub * EPL;
+    const T* qrow = static_cast<const T*>(p.q) + p.sq.head(b, h) + (int64_t)i * p.sq.s;
+    const T* kb = static_cast<const T*>(p.k) + p.sk.head(b, h) + sub * EPL;
+    const T* vb = static_cast<const T*>(p.v) + p.sk.head(b, h) + sub * EPL;
 
     float qf[EPL];
     {
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(128) void splitk_merge_kernel(SplitParams p) {
     }
     if (t < D) {
         const float out = L > 0.f ? A / L : 0.f;
-        T* orow = static_cast<T*>(p.o) + b * p.sq.b + h * p.sq.h + (int64_t)i * p.sq.s;
+        T* orow = static_cast<T*>(p.o) + p.sq.head(b, h) + (int64_t)i * p.sq.s;
         orow[t] = to_storage<Tag>(out);
     }
     if (t == 0 && p.lse != nullptr) p.lse[row] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;

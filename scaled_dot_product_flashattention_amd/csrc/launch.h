@@ -18,7 +18,7 @@ struct FwdArgs {
     int B, H, Sq, Sk, d;
     float scale;
     int causal;
-    int layout;  // 0 = [B,H,S,d], 1 = [B,S,H,d]
+    int layout;  // 0 = [B,H,S,d], 1 = [B,S,H,d], 0x10000 | g = groups of g heads
     int dtype;   // 0 = fp32, 1 = fp16, 2 = bf16
 };
 
@@ -38,7 +38,7 @@ struct QkvArgs {
     void* k;
     void* v;
     int B, S, D, H, d;
-    int layout;  // 0 = [B,H,S,d], 1 = [B,S,H,d]
+    int layout;  // as FwdArgs::layout
     int dtype;   // 1 = fp16, 2 = bf16
 };
 hipError_t run_qkv_proj(const QkvArgs& a, hipStream_t stream);

@@ -63,8 +63,8 @@ __global__ __launch_bounds__(256) void naive_scores_kernel(NaiveParams p) {
     const int bh = w / p.n_qtiles;
     const int b = bh / p.H, h = bh % p.H;
     const int nb = clamp_len(p.kv_len, b, p.Sk);
-    const T* qp = static_cast<const T*>(p.q) + b * p.sq.b + h * p.sq.h;
-    const T* kp = static_cast<const T*>(p.k) + b * p.sk.b + h * p.sk.h;
+    const T* qp = static_cast<const T*>(p.q) + p.sq.head(b, h);
+    const T* kp = static_cast<const T*>(p.k) + p.sk.head(b, h);
 
     for (int idx = tid; idx < BN * CPR; idx += 256) {
         const int row = idx / CPR, cc = idx % CPR;
@@ -178,8 +178,8 @@ __global__ __launch_bounds__(256) void naive_pv_kernel(NaiveParams p) {
     const int nb = clamp_len(p.kv_len, b, p.Sk);
     const int q_end = min((qt + 1) * BM, p.Sq);
     const int kend = p.causal ? min(nb, q_end) : nb;
-    const T* vp = static_cast<const T*>(p.v) + b * p.sk.b + h * p.sk.h;
-    T* op = static_cast<T*>(p.o) + b * p.sq.b + h * p.sq.h;
+    const T* vp = static_cast<const T*>(p.v) + p.sk.head(b, h);
+    T* op = static_cast<T*>(p.o) + p.sq.head(b, h);
     const int qw0 = qt * BM + wave * 32;
     const int qi = qw0 + n32;
     const bool ok = qi < p.Sq;

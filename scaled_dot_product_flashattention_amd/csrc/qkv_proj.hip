@@ -5,8 +5,9 @@
 // projections X W_Q, X W_K and X W_V are done as one product with the three
 // weights side by side ([D, 3 Hd]) and then split. Here the split is part of
 // the store: output column n = t*Hd + h*d + c goes to tensor t (Q, K, V),
-// head h, dimension c, in the layout the attention kernel reads ([B,H,S,d] or
-// [B,S,H,d], page "WebGPU 算子优化…", section "QKV 矩阵的内存合并模式选择").
+// head h, dimension c, in the layout the attention kernel reads ([B,H,S,d],
+// [B,S,H,d] or the head-group split, page "WebGPU 算子优化…", section "QKV
+// 矩阵的内存合并模式选择").
 //
 // Y = X W^T with X [M = B*S, K = D] and the weight stored out-major,
 // w[n][i] (as a linear layer keeps it), so both operands of the matrix
@@ -49,7 +50,7 @@ struct QkvParams {
     void* out[3];
     int M, N, K;   // B*S, 3*H*d, D
     int S, H, d;
-    int layout;    // 0 [B,H,S,d], 1 [B,S,H,d]
+    Strides so;    // output layout
     int n_ntiles;  // column tiles
 };
 
@@ -179,8 +180,7 @@ __global__ __launch_bounds__(QNT, 2) void qkv_proj_kernel(QkvParams p) {
         const int t = n / HD, j = n - t * HD;
         const int h = j / p.d, c = j - h * p.d;
         const int b = m / p.S, s = m - b * p.S;
-        const int64_t dst = p.layout == 0 ? (((int64_t)b * p.H + h) * p.S + s) * p.d + c
-                                          : (int64_t)m * HD + j;
+        const int64_t dst = p.so.head(b, h) + (int64_t)s * p.so.s + c;
         *reinterpret_cast<u32x4*>(static_cast<T*>(p.out[t]) + dst) =
             *reinterpret_cast<const u32x4*>(Ys + row * QOROW + cc * 8);
     }
@@ -201,7 +201,7 @@ hipError_t run_qkv_proj(const QkvArgs& a, hipStream_t stream) {
     p.S = a.S;
     p.H = a.H;
     p.d = a.d;
-    p.layout = a.layout;
+    p.so = make_strides(a.layout, a.H, a.S, a.d);
     p.n_ntiles = (p.N + QBN - 1) / QBN;
     const int64_t grid = (int64_t)((p.M + QBM - 1) / QBM) * p.n_ntiles;
     if (grid > 0x7fffffff || grid == 0) return grid == 0 ? hipSuccess : hipErrorInvalidValue;

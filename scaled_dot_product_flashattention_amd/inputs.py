@@ -36,7 +36,7 @@ class Workload:
     Sk: int
     d: int
     dtype: str            # "f32" | "f16" | "bf16"
-    layout: str           # "bhsd" | "bshd"
+    layout: str           # "bhsd" | "bshd" | "split:g"
     causal: bool = False
     qk_mult: float = 1.0  # multiplier applied to q and k before the cast
     kv_len_range: tuple[int, int] | None = None  # inclusive range of valid key counts
@@ -47,10 +47,13 @@ class Workload:
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
 
-    def shape(self, S: int) -> tuple[int, int, int, int]:
+    def shape(self, S: int) -> tuple:
         if self.layout == "bhsd":
             return (self.B, self.H, S, self.d)
-        return (self.B, S, self.H, self.d)
+        if self.layout == "bshd":
+            return (self.B, S, self.H, self.d)
+        g = int(self.layout.split(":")[1])  # "split:g": heads in groups of g
+        return (self.B, self.H // g, S, g, self.d)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -123,9 +126,9 @@ def poison_padding(k: torch.Tensor, v: torch.Tensor, kv_len, layout: str) -> Non
     if kv_len is None:
         return
     for b, n in enumerate(torch.as_tensor(kv_len).tolist()):
-        if layout == "bhsd":
-            k[b, :, n:, :] = float("nan")
-            v[b, :, n:, :] = float("nan")
-        else:
-            k[b, n:, :, :] = float("nan")
-            v[b, n:, :, :] = float("nan")
+        if layout == "bshd":
+            k[b, n:] = float("nan")
+            v[b, n:] = float("nan")
+        else:  # [B, H, S, d] or [B, H/g, S, g, d]: rows are the third index
+            k[b, :, n:] = float("nan")
+            v[b, :, n:] = float("nan")

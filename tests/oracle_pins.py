@@ -539,6 +539,35 @@ def pin_softmax_rows_torch(orc):
         close(lse, torch.logsumexp(xs, dim=1).numpy(), 1e-12, f"lse vs torch {dt}")
 
 
+
+def _split_from_bhsd(x: np.ndarray, g: int) -> np.ndarray:
+    """[B, H, S, d] -> [B, H/g, S, g, d] (groups of g heads)."""
+    B, H, S, d = x.shape
+    return np.ascontiguousarray(x.reshape(B, H // g, g, S, d).transpose(0, 1, 3, 2, 4))
+
+
+def pin_split_layout(orc):
+    """The page's head-group ("Split") layout [B, H/g, S, g, d] holds the same
+    heads: attention and the QKV projection in it equal their [B,H,S,d]
+    results moved to that order, exactly, for g = 1, 2 and H."""
+    rng = np.random.default_rng(41)
+    B, H, S, d = 2, 4, 9, 8
+    q, k, v = (rand(rng, (B, H, S, d)) for _ in range(3))
+    o_ref, lse_ref = orc.attention(q, k, v, scale=0.3, causal=True, layout="bhsd", kv_len=[9, 5])
+    for g in (1, 2, H):
+        qs, ks, vs = (_split_from_bhsd(x, g) for x in (q, k, v))
+        o, lse = orc.attention(qs, ks, vs, scale=0.3, causal=True, layout=f"split:{g}", kv_len=[9, 5])
+        assert np.array_equal(o, _split_from_bhsd(o_ref, g)), f"split:{g} attention"
+        assert np.array_equal(lse, lse_ref), f"split:{g} lse"
+    x = rand(rng, (B, S, 16))
+    w = rand(rng, (3 * H * d, 16))
+    ref = orc.qkv_proj(x, w, H=H, d=d, layout="bhsd")
+    for g in (1, 2, H):
+        got = orc.qkv_proj(x, w, H=H, d=d, layout=f"split:{g}")
+        for t in range(3):
+            assert np.array_equal(got[t], _split_from_bhsd(ref[t], g)), f"split:{g} projection {t}"
+
+
 ALL_PINS = [
     pin_decode_exact,
     pin_rows_sum_to_one,
@@ -558,4 +587,5 @@ ALL_PINS = [
     pin_qkv_library,
     pin_softmax_rows_closed_forms,
     pin_softmax_rows_torch,
+    pin_split_layout,
 ]

@@ -114,7 +114,13 @@ def sampled_case(w: Workload, path="fused", n_rows=48, n_split=None, seed=None):
     got_l = np.empty_like(lse_ref)
     for n, r in enumerate(rows):
         i, h, b = r % w.Sq, (r // w.Sq) % w.H, r // (w.Sq * w.H)
-        got[n] = (o_c[b, h, i] if w.layout == "bhsd" else o_c[b, i, h]).numpy()
+        if w.layout == "bhsd":
+            got[n] = o_c[b, h, i].numpy()
+        elif w.layout == "bshd":
+            got[n] = o_c[b, i, h].numpy()
+        else:
+            g = o_c.shape[3]
+            got[n] = o_c[b, h // g, i, h % g].numpy()
         got_l[n] = lse_c[b, h, i]
     both_inf = np.isneginf(got_l) & np.isneginf(lse_ref)
     with np.errstate(invalid="ignore"):

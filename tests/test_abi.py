@@ -17,6 +17,10 @@ HEADER = os.path.join(ROOT, "include", "attn.h")
 
 OK, E_NULLPTR, E_SHAPE, E_UNSUPPORTED, E_ALIGN, E_WORKSPACE, E_HIP, E_ARG = range(8)
 BHSD, BSHD = 0, 1
+
+
+def SPLIT(g):  # heads in groups of g
+    return 0x10000 | g
 F32, F16, BF16 = 0, 1, 2
 
 # fake, never dereferenced device addresses (validation fails before any use)
@@ -75,7 +79,8 @@ def test_validation_statuses(lib, fn):
                 dict(B=1 << 16, H=1 << 10, Sq=1 << 10)):
         assert call(lib, fn, **bad) == E_SHAPE, bad
     for bad in (dict(d=96), dict(d=256), dict(d=0), dict(layout=2), dict(layout=-1),
-                dict(dtype=3), dict(dtype=-1)):
+                dict(dtype=3), dict(dtype=-1), dict(layout=SPLIT(3)), dict(layout=SPLIT(0)),
+                dict(layout=SPLIT(4)), dict(layout=0x20000 | 2)):
         assert call(lib, fn, **bad) == E_UNSUPPORTED, bad
     for bad in (float("nan"), float("inf"), float("-inf"), -0.5):
         assert call(lib, fn, scale=bad) == E_ARG, bad
@@ -142,7 +147,7 @@ def test_qkv_proj_validation(lib):
     for bad in (dict(B=0), dict(S=0), dict(H=0), dict(D=0), dict(D=96), dict(D=32), dict(d=0),
                 dict(d=12), dict(B=1 << 16, S=1 << 16)):
         assert qkv(lib, **bad) == E_SHAPE, bad
-    for bad in (dict(dtype=F32), dict(dtype=5), dict(layout=2)):
+    for bad in (dict(dtype=F32), dict(dtype=5), dict(layout=2), dict(layout=SPLIT(3))):
         assert qkv(lib, **bad) == E_UNSUPPORTED, bad
     for bad in (dict(x=A16 + 8), dict(w=A16 + 2), dict(q=A16_2 + 4), dict(v=A16_2 + 8)):
         assert qkv(lib, **bad) == E_ALIGN, bad
@@ -173,3 +178,15 @@ def test_python_binding_rejects_host_tensors(lib):
     with pytest.raises(sdpa.AttnError) as ei:
         sdpa.attn_fwd_plan(1, 1, 1, 1, 96, torch.bfloat16)
     assert ei.value.status == E_UNSUPPORTED
+
+
+def test_layout_names():
+    """The binding's layout names map to the header's codes and tensor shapes."""
+    from scaled_dot_product_flashattention_amd.api import layout_code, layout_shape
+    assert layout_code("bhsd") == 0 and layout_code("bshd") == 1
+    assert layout_code("split:4") == SPLIT(4)
+    assert layout_shape("bhsd", 2, 8, 5, 64) == (2, 8, 5, 64)
+    assert layout_shape("bshd", 2, 8, 5, 64) == (2, 5, 8, 64)
+    assert layout_shape("split:4", 2, 8, 5, 64) == (2, 2, 5, 4, 64)
+    with pytest.raises(ValueError):
+        layout_code("bsdh")

@@ -49,6 +49,8 @@ MUTANTS = {
     "softmax rows lse without max": ("lse[r] = m + log(l);", "lse[r] = log(l);"),
     "softmax rows masked kept": ("yr[j] = v == -INFINITY ? 0.0 : exp(scale * v - m);",
                                  "yr[j] = v == -INFINITY ? 1e-30 : exp(scale * v - m);"),
+    "split groups transposed": ("return (((b * (H / g) + h / g) * S + s) * g + h % g) * d + c;",
+                                "return (((b * (H / g) + h % (H / g)) * S + s) * g + h / (H / g)) * d + c;"),
 }
 
 

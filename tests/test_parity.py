@@ -100,3 +100,29 @@ def test_long_keys_head64(dtype, layout, causal, pad):
                                  dtype=dtype, layout=layout, causal=causal,
                                  kv_len_range=(1500, 2300) if pad else None, seed=31)
     full_case(w, poison=pad)
+
+
+@pytest.mark.parametrize("g", [1, 2, 4])
+@pytest.mark.parametrize("dtype,d,Sk", [("bf16", 64, 300), ("bf16", 64, 2200), ("f16", 128, 300),
+                                         ("f32", 64, 200)])
+def test_split_layout(g, dtype, d, Sk):
+    """The page's head-group layout [B, H/g, S, g, d] (ATTN_LAYOUT_SPLIT(g)),
+    with padding and causal rows, on every kernel shape (4-wave and 8-wave
+    16-bit, fp32)."""
+    w = W["medium_bf16"].replace(name=f"split{g}", B=2, H=4, Sq=Sk if Sk < 1000 else 260, Sk=Sk,
+                                 d=d, dtype=dtype, layout=f"split:{g}", causal=(g == 2),
+                                 kv_len_range=(Sk // 2, Sk), seed=50 + g)
+    full_case(w, poison=True)
+
+
+@pytest.mark.parametrize("path", ["splitk", "naive"])
+def test_split_layout_other_paths(path):
+    w = W["decode_bf16"].replace(name="split_dec", B=2, H=4, Sq=1 if path == "splitk" else 100,
+                                 Sk=3000, layout="split:2", seed=61)
+    full_case(w, path=path, n_split=6 if path == "splitk" else None)
+
+
+def test_split_layout_full_size_sampled():
+    """Medium prefill shape (B1 H16 S4096 d64 bf16) in groups of 4 heads, at
+    full size, on sampled rows."""
+    sampled_case(W["medium_bf16"].replace(name="medium_split4", layout="split:4"))

@@ -42,11 +42,13 @@ SHAPES = [  # (B, S, D, H, d): column tails, row tails, one and several K steps
 ]
 
 
-@pytest.mark.parametrize("layout", ["bhsd", "bshd"])
+@pytest.mark.parametrize("layout", ["bhsd", "bshd", "split:2"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", [s for s in SHAPES], ids=lambda s: "x".join(map(str, s)))
 def test_qkv_proj_matches_oracle(shape, dtype, layout):
     B, S, D, H, d = shape
+    if layout.startswith("split") and H % 2:
+        layout = f"split:{H}"
     say(f"qkv_proj B{B} S{S} D{D} H{H} d{d} {dtype} {layout}")
     t = generate_qkv_proj(B, S, D, H, d, dtype, seed=B * 1000 + S + D + d)
     want = oracle.qkv_proj(t["x"], t["w"], H=H, d=d, layout=layout)
