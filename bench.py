@@ -261,11 +261,15 @@ def main() -> int:
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
     kw = dict(scale=w.scale, causal=w.causal, layout=w.layout, kv_len=kv_len, out=o, lse=lse)
+    tile = None
     if args.path == "fused":
         nbytes = sdpa.attn_fwd_workspace_size(B, H, Sq, Sk, d, q.dtype)
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
         step = lambda: sdpa.attn_fwd(q, k, v, workspace=ws, **kw)  # noqa: E731
         n_split = sdpa.attn_fwd_plan(B, H, Sq, Sk, d, q.dtype)
+        if n_split == 1:
+            t_id = sdpa.attn_fwd_tile_choice(B, H, Sq, Sk, d, q.dtype, w.causal)
+            tile = {"variant": t_id, **sdpa.attn_fwd_tile_info(d, q.dtype, t_id)}
     elif args.path == "splitk":
         n_split = args.n_split or sdpa.attn_fwd_plan(B, H, Sq, Sk, d, q.dtype)
         ws = torch.empty(sdpa.attn_splitk_workspace_size(B, H, Sq, d, n_split), dtype=torch.uint8,
@@ -339,7 +343,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "B": B, "H": H, "Sq": Sq,
                    "Sk": Sk, "d": d, "layout": w.layout, "causal": w.causal, "path": args.path,
-                   "n_split": n_split, "flops_per_step": fl, "wall_ms_timed_region": round(wall_ms, 2),
+                   "n_split": n_split, "tile": tile, "flops_per_step": fl, "wall_ms_timed_region": round(wall_ms, 2),
                    "peak_device_bytes": peak_bytes},
         "roofline": roof,
     }

@@ -64,7 +64,7 @@ enum attn_status {
     ATTN_E_ALIGN = 4,       /* a pointer is not aligned as stated above          */
     ATTN_E_WORKSPACE = 5,   /* workspace / scratch NULL or smaller than required */
     ATTN_E_HIP = 6,         /* the HIP runtime reported an error at launch       */
-    ATTN_E_ARG = 7          /* scale is negative, NaN or infinite                */
+    ATTN_E_ARG = 7          /* scale negative, NaN or infinite; tile out of range */
 };
 
 enum attn_layout { ATTN_LAYOUT_BHSD = 0, ATTN_LAYOUT_BSHD = 1 };
@@ -96,6 +96,46 @@ size_t attn_fwd_workspace_size(int B, int H, int Sq, int Sk, int d, int dtype);
 /* The number of key splits attn_fwd will use (1 = single fused kernel).
  * Host only; returns a status and writes *n_split on success. */
 int attn_fwd_plan(int B, int H, int Sq, int Sk, int d, int dtype, int* n_split);
+
+/*
+ * Tile variants of the fused kernel. The WebGPU page's section
+ * "浏览器端落地的关键参数与监控" picks the sequence and head-dimension tiles
+ * per device by a probe at the first run, falling back to smaller tiles. Here
+ * the candidates are compiled in, and the choice is a table made offline by
+ * timing every candidate on the GPU over a grid of query-row counts
+ * (B*H*Sq) and key lengths, per head size and masking (the package's
+ * autotune script writes it; the library must be rebuilt to use a new one).
+ * attn_fwd and the prefill part of its plan use the table's choice.
+ */
+typedef struct attn_tile_info {
+    int rows;      /* query rows per workgroup                              */
+    int keys;      /* keys per tile of the LDS ring                         */
+    int waves;     /* 64-lane waves per workgroup                           */
+    int stages;    /* LDS ring stages                                       */
+    int lds_bytes; /* LDS per workgroup                                     */
+} attn_tile_info;
+
+/* Number of tile variants for (d, dtype); 0 when the pair is unsupported.
+ * Host only. */
+int attn_fwd_tile_count(int d, int dtype);
+
+/* Describe variant `tile` (0 <= tile < attn_fwd_tile_count) in *info.
+ * Returns ATTN_E_NULLPTR, ATTN_E_UNSUPPORTED for a bad d or dtype, ATTN_E_ARG
+ * for a tile out of range. Host only. */
+int attn_fwd_tile_info(int d, int dtype, int tile, attn_tile_info* info);
+
+/* The variant the table picks for this shape, in *tile. Host only. */
+int attn_fwd_tile_choice(int B, int H, int Sq, int Sk, int d, int dtype, int causal, int* tile);
+
+/*
+ * The fused single-kernel forward with tile variant `tile` (-1: the table's
+ * choice), whatever the shape: never the split path, no workspace. Same
+ * arguments and results as attn_fwd otherwise; a tile out of range is
+ * ATTN_E_ARG. For tuning and testing every variant.
+ */
+int attn_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
+                   int dtype, const int32_t* kv_len, int tile, void* stream);
 
 /*
  * Split-over-keys forward with an explicit split count (the single-query

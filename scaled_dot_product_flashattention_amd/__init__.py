@@ -11,6 +11,10 @@ from .api import (  # noqa: F401
     attn_fwd_naive,
     attn_fwd_plan,
     attn_fwd_splitk,
+    attn_fwd_tile_choice,
+    attn_fwd_tile_count,
+    attn_fwd_tile_info,
+    attn_fwd_tiled,
     attn_fwd_workspace_size,
     attn_naive_scratch_size,
     attn_qkv_proj,

@@ -38,6 +38,12 @@ def layout_shape(layout: str, B: int, H: int, S: int, d: int) -> tuple:
     return (B, H // g, S, g, d)
 
 
+class TileInfo(ctypes.Structure):
+    """attn_tile_info of attn.h: one tile variant of the fused kernel."""
+    _fields_ = [("rows", ctypes.c_int), ("keys", ctypes.c_int), ("waves", ctypes.c_int),
+                ("stages", ctypes.c_int), ("lds_bytes", ctypes.c_int)]
+
+
 class AttnError(RuntimeError):
     """A libattn call returned a nonzero status."""
 
@@ -79,6 +85,14 @@ def load_library() -> ctypes.CDLL:
     L.attn_qkv_proj.restype = i
     L.attn_softmax_rows.argtypes = [vp, vp, vp, ctypes.c_int64, i, f, i, i, vp]
     L.attn_softmax_rows.restype = i
+    L.attn_fwd_tile_count.argtypes = [i, i]
+    L.attn_fwd_tile_count.restype = i
+    L.attn_fwd_tile_info.argtypes = [i, i, i, ctypes.POINTER(TileInfo)]
+    L.attn_fwd_tile_info.restype = i
+    L.attn_fwd_tile_choice.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i)]
+    L.attn_fwd_tile_choice.restype = i
+    L.attn_fwd_tiled.argtypes = tensors + [i, vp]
+    L.attn_fwd_tiled.restype = i
     L.attn_status_string.argtypes = [i]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_version.argtypes = []
@@ -108,6 +122,28 @@ def attn_fwd_plan(B: int, H: int, Sq: int, Sk: int, d: int, dtype: torch.dtype) 
     if rc:
         raise AttnError("attn_fwd_plan", rc)
     return n.value
+
+
+def attn_fwd_tile_count(d: int, dtype: torch.dtype) -> int:
+    return load_library().attn_fwd_tile_count(d, dtype_code(dtype))
+
+
+def attn_fwd_tile_info(d: int, dtype: torch.dtype, tile: int) -> dict:
+    info = TileInfo()
+    rc = load_library().attn_fwd_tile_info(d, dtype_code(dtype), tile, ctypes.byref(info))
+    if rc:
+        raise AttnError("attn_fwd_tile_info", rc)
+    return {name: getattr(info, name) for name, _ in TileInfo._fields_}
+
+
+def attn_fwd_tile_choice(B: int, H: int, Sq: int, Sk: int, d: int, dtype: torch.dtype,
+                         causal: bool = False) -> int:
+    t = ctypes.c_int(-1)
+    rc = load_library().attn_fwd_tile_choice(B, H, Sq, Sk, d, dtype_code(dtype), int(bool(causal)),
+                                             ctypes.byref(t))
+    if rc:
+        raise AttnError("attn_fwd_tile_choice", rc)
+    return t.value
 
 
 def attn_fwd_workspace_size(B: int, H: int, Sq: int, Sk: int, d: int, dtype: torch.dtype) -> int:
@@ -200,6 +236,21 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, layout="bhsd", kv_len=None, r
                                  _stream(q, stream))
     if rc:
         raise AttnError("attn_fwd", rc)
+    return o, lse
+
+
+def attn_fwd_tiled(q, k, v, *, tile=-1, scale=None, causal=False, layout="bhsd", kv_len=None,
+                   return_lse=True, out=None, lse=None, stream=None):
+    """The fused kernel with tile variant ``tile`` (-1: the tuned table's
+    choice), never the split path. Returns (o, lse)."""
+    (B, H, Sq, Sk, d), kv_len, scale, o, lse = _prepare(q, k, v, layout, kv_len, scale, lse,
+                                                        return_lse, out)
+    rc = load_library().attn_fwd_tiled(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq, Sk,
+                                       d, scale, int(bool(causal)), layout_code(layout),
+                                       dtype_code(q.dtype), _ptr(kv_len), int(tile),
+                                       _stream(q, stream))
+    if rc:
+        raise AttnError("attn_fwd_tiled", rc)
     return o, lse
 
 

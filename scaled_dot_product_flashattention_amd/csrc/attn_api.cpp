@@ -141,6 +141,44 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
     return status_of(attn::run_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
+int attn_fwd_tile_count(int d, int dtype) {
+    if (check_shape(1, 1, 1, 1, d, ATTN_LAYOUT_BHSD, dtype) != ATTN_OK) return 0;
+    return attn::prefill_tile_count(d, dtype);
+}
+
+int attn_fwd_tile_info(int d, int dtype, int tile, attn_tile_info* info) {
+    if (!info) return ATTN_E_NULLPTR;
+    int rc = check_shape(1, 1, 1, 1, d, ATTN_LAYOUT_BHSD, dtype);
+    if (rc != ATTN_OK) return rc;
+    attn::TileInfo t;
+    if (!attn::prefill_tile_info(d, dtype, tile, &t)) return ATTN_E_ARG;
+    info->rows = t.rows;
+    info->keys = t.keys;
+    info->waves = t.waves;
+    info->stages = t.stages;
+    info->lds_bytes = t.lds_bytes;
+    return ATTN_OK;
+}
+
+int attn_fwd_tile_choice(int B, int H, int Sq, int Sk, int d, int dtype, int causal, int* tile) {
+    if (!tile) return ATTN_E_NULLPTR;
+    int rc = check_shape(B, H, Sq, Sk, d, ATTN_LAYOUT_BHSD, dtype);
+    if (rc != ATTN_OK) return rc;
+    *tile = attn::prefill_tile_choice(B, H, Sq, Sk, d, dtype, causal != 0);
+    return ATTN_OK;
+}
+
+int attn_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
+                   int dtype, const int32_t* kv_len, int tile, void* stream) {
+    int rc = check_call(q, k, v, o, lse, B, H, Sq, Sk, d, scale, layout, dtype, kv_len);
+    if (rc != ATTN_OK) return rc;
+    if (tile < -1 || tile >= attn::prefill_tile_count(d, dtype)) return ATTN_E_ARG;
+    attn::FwdArgs a = make_args(q, k, v, o, lse, B, H, Sq, Sk, d, scale, causal, layout, dtype, kv_len);
+    a.tile = tile;
+    return status_of(attn::run_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t attn_naive_scratch_size(int B, int H, int Sq, int Sk, int dtype) {
     if (check_shape(B, H, Sq, Sk, 64, ATTN_LAYOUT_BHSD, dtype) != ATTN_OK) return 0;
     return attn::naive_scratch_bytes(B, H, Sq, Sk, dtype);

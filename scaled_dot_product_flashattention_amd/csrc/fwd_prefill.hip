@@ -472,7 +472,26 @@ hipError_t launch_prefill(const FwdArgs& a, hipStream_t stream) {
 
 hipError_t run_prefill(const FwdArgs& a, hipStream_t stream) {
     if (a.dtype != 0) return run_prefill16(a, stream);
+    if (a.tile > 0) return hipErrorInvalidValue;  // fp32 has one variant
     return a.d == 64 ? launch_prefill<F32, 64, 1, false>(a, stream) : launch_prefill<F32, 128, 1, false>(a, stream);
+}
+
+// fp32 inputs have a single tile variant per head size.
+int prefill_tile_count(int d, int dtype) { return dtype == 0 ? 1 : prefill16_tile_count(d); }
+
+bool prefill_tile_info(int d, int dtype, int tile, TileInfo* out) {
+    if (dtype != 0) return prefill16_tile_info(d, tile, out);
+    if (tile != 0 || (d != 64 && d != 128)) return false;
+    out->rows = PrefillCfg<F32, 64, 1>::BM;
+    out->keys = PrefillCfg<F32, 64, 1>::BN;
+    out->waves = PrefillCfg<F32, 64, 1>::NW;
+    out->stages = 2;
+    out->lds_bytes = d == 64 ? PrefillCfg<F32, 64, 1>::LDS_BYTES : PrefillCfg<F32, 128, 1>::LDS_BYTES;
+    return true;
+}
+
+int prefill_tile_choice(int B, int H, int Sq, int Sk, int d, int dtype, int causal) {
+    return dtype == 0 ? 0 : prefill16_tile_choice(B, H, Sq, Sk, d, causal);
 }
 
 }  // namespace attn

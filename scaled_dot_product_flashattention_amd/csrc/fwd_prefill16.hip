@@ -75,6 +75,17 @@ struct Prefill16Params {
     int remap;  // grid size is a multiple of 8: keep each head's tiles on one XCD
 };
 
+// LDS of one workgroup: the K/V ring, reused for the output staging rows
+// (D + 8 elements per query) and, with two key halves, for the merge of the
+// halves' (O, m, l) in fp32.
+constexpr int lds_bytes16(int D, int NQ, int BN, int NST, int KSPLIT) {
+    const int ring = NST * 2 * BN * D * 2;
+    const int out = 4 * 32 * NQ * (D + 8) * 2;
+    const int mrg = KSPLIT == 2 ? 4 * (NQ * (D / 32) * 16 + 2 * NQ) * 64 * 4 : 0;
+    const int a = ring > out ? ring : out;
+    return a > mrg ? a : mrg;
+}
+
 // XOR swizzle of the 16-byte chunks of LDS row `row` (see the header comment).
 template <int D> __device__ __forceinline__ int swz_k(int row) {
     return D == 64 ? ((row >> 1) & 7) : (row & 15);
@@ -131,11 +142,8 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
     constexpr int DPT = 2 * DMA1;                  // ... for K and V
     constexpr int P = NST - 2;                     // tiles issued ahead
     constexpr int OROW = D + 8;                    // output staging row (elements)
-    constexpr int OUT_B = 4 * 32 * NQ * OROW * 2;
     constexpr int MRG_W = (NQ * (D / 32) * 16 + 2 * NQ) * 64 * 4;  // one wave's (O, m, l) in fp32
-    constexpr int MRG_B = KSPLIT == 2 ? 4 * MRG_W : 0;
-    constexpr int LDS_A = NST * STAGE_B > OUT_B ? NST * STAGE_B : OUT_B;
-    constexpr int LDS_B = LDS_A > MRG_B ? LDS_A : MRG_B;
+    constexpr int LDS_B = lds_bytes16(D, NQ, BN, NST, KSPLIT);
     constexpr int NPV = KBW * 2 * (D / 32) * NQ;   // products of P V per tile and wave
     constexpr int NQK = (D / 16) * KBW * NQ;       // products of K Q^T per tile and wave
     constexpr int NM = NPV + NQK;
@@ -592,27 +600,77 @@ hipError_t launch16(const FwdArgs& a, hipStream_t stream) {
     const int64_t grid = (int64_t)p.n_qtiles * a.B * a.H;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     p.remap = (grid % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((fwd_prefill16_kernel<Tag, D, NQ, BN, NST, KSPLIT>), dim3((unsigned)grid), dim3(256 * KSPLIT), 0,
-                       stream, p);
+    hipLaunchKernelGGL((fwd_prefill16_kernel<Tag, D, NQ, BN, NST, KSPLIT>), dim3((unsigned)grid),
+                       dim3(256 * KSPLIT), 0, stream, p);
     return hipGetLastError();
+}
+
+// ---- tile variants and their choice ----------------------------------------
+// Tile sizes are not probed at run time: the candidates below are compiled in
+// (each without register spills at two waves per SIMD), and a table made
+// offline by timing every candidate over a grid of shapes (tile_table.inc)
+// names the variant per head size, masking, key length and query rows.
+struct Variant16 {
+    int nq, bn, nst, ksplit, lds;
+    hipError_t (*run[2])(const FwdArgs&, hipStream_t);  // fp16, bf16
+};
+#define ATTN_VARIANT16(D, NQ, BN, NST, KS)                                       \
+    {NQ, BN, NST, KS, lds_bytes16(D, NQ, BN, NST, KS),                           \
+     {&launch16<F16, D, NQ, BN, NST, KS>, &launch16<BF16, D, NQ, BN, NST, KS>}}
+const Variant16 kVariants64[] = {
+    ATTN_VARIANT16(64, 1, 64, 5, 1),  // 0: 128 queries x 64 keys, 4 waves
+    ATTN_VARIANT16(64, 1, 64, 4, 1),  // 1: same, shorter ring
+    ATTN_VARIANT16(64, 2, 64, 8, 2),  // 2: 256 queries, 8 waves in two key halves
+    ATTN_VARIANT16(64, 1, 64, 8, 2),  // 3: 128 queries, 8 waves in two key halves
+};
+const Variant16 kVariants128[] = {
+    ATTN_VARIANT16(128, 1, 32, 5, 1),  // 0: 128 queries x 32 keys, 4 waves
+    ATTN_VARIANT16(128, 1, 32, 4, 1),  // 1: same, shorter ring
+    ATTN_VARIANT16(128, 1, 64, 4, 2),  // 2: 128 queries x 64 keys, 8 waves in two key halves
+    ATTN_VARIANT16(128, 1, 64, 5, 2),  // 3: same, deeper ring (all 160 KiB of LDS)
+};
+#undef ATTN_VARIANT16
+constexpr int kNumVariants64 = sizeof(kVariants64) / sizeof(kVariants64[0]);
+constexpr int kNumVariants128 = sizeof(kVariants128) / sizeof(kVariants128[0]);
+
+#include "tile_table.inc"
+
+// Bucket of x on a log2 grid starting at 2^lo with n points (nearest point).
+int log2_bucket(int64_t x, int lo, int n) {
+    int e = 0;
+    while (e < 62 && (int64_t(1) << (e + 1)) <= x) ++e;  // floor(log2 x)
+    // round: x >= 2^e * sqrt(2) goes up
+    if (e < 62 && (double)x >= (double)(int64_t(1) << e) * 1.4142135623730951) ++e;
+    const int i = e - lo;
+    return i < 0 ? 0 : (i >= n ? n - 1 : i);
 }
 
 }  // namespace
 
-// Kernel choice (measured on MI355X): head size 64 over long key ranges uses
-// 8 waves in two key halves (half the LDS operand traffic per product);
-// short key ranges, where the longer pipeline fill and the final merge do not
-// pay off, and head size 128 use 4 waves.
-constexpr int kKeySplitMinKeys = 2048;
+int prefill16_tile_count(int d) { return d == 64 ? kNumVariants64 : d == 128 ? kNumVariants128 : 0; }
+
+bool prefill16_tile_info(int d, int tile, TileInfo* out) {
+    if (tile < 0 || tile >= prefill16_tile_count(d)) return false;
+    const Variant16& v = d == 64 ? kVariants64[tile] : kVariants128[tile];
+    out->rows = 4 * 32 * v.nq;
+    out->keys = v.bn;
+    out->waves = 4 * v.ksplit;
+    out->stages = v.nst;
+    out->lds_bytes = v.lds;
+    return true;
+}
+
+int prefill16_tile_choice(int B, int H, int Sq, int Sk, int d, int causal) {
+    const int r = log2_bucket((int64_t)B * H * Sq, kTuneRowsLog2Min, kTuneRowsBuckets);
+    const int k = log2_bucket(Sk, kTuneKeysLog2Min, kTuneKeysBuckets);
+    return kTileTable[d == 128 ? 1 : 0][causal ? 1 : 0][r][k];
+}
 
 hipError_t run_prefill16(const FwdArgs& a, hipStream_t stream) {
-    const bool ks = a.d == 64 && a.Sk >= kKeySplitMinKeys;
-    if (a.dtype == 2) {
-        if (a.d == 128) return launch16<BF16, 128, 1, 32, 5, 1>(a, stream);
-        return ks ? launch16<BF16, 64, 2, 64, 8, 2>(a, stream) : launch16<BF16, 64, 1, 64, 5, 1>(a, stream);
-    }
-    if (a.d == 128) return launch16<F16, 128, 1, 32, 5, 1>(a, stream);
-    return ks ? launch16<F16, 64, 2, 64, 8, 2>(a, stream) : launch16<F16, 64, 1, 64, 5, 1>(a, stream);
+    const int tile = a.tile >= 0 ? a.tile : prefill16_tile_choice(a.B, a.H, a.Sq, a.Sk, a.d, a.causal);
+    if (tile < 0 || tile >= prefill16_tile_count(a.d)) return hipErrorInvalidValue;
+    const Variant16& v = a.d == 128 ? kVariants128[tile] : kVariants64[tile];
+    return v.run[a.dtype == 2 ? 1 : 0](a, stream);
 }
 
 }  // namespace attn

@@ -18,13 +18,25 @@ struct FwdArgs {
     int B, H, Sq, Sk, d;
     float scale;
     int causal;
-    int layout;  // 0 = [B,H,S,d], 1 = [B,S,H,d], 0x10000 | g = groups of g heads
-    int dtype;   // 0 = fp32, 1 = fp16, 2 = bf16
+    int layout;     // 0 = [B,H,S,d], 1 = [B,S,H,d], 0x10000 | g = groups of g heads
+    int dtype;      // 0 = fp32, 1 = fp16, 2 = bf16
+    int tile = -1;  // fused kernel's tile variant; -1 = the tuned table's choice
 };
 
 // Fused single-kernel forward (any shape); 16-bit inputs go to run_prefill16.
 hipError_t run_prefill(const FwdArgs& a, hipStream_t stream);
 hipError_t run_prefill16(const FwdArgs& a, hipStream_t stream);
+
+// Tile variants of the fused kernel (as attn_tile_info in attn.h).
+struct TileInfo {
+    int rows, keys, waves, stages, lds_bytes;
+};
+int prefill_tile_count(int d, int dtype);
+bool prefill_tile_info(int d, int dtype, int tile, TileInfo* out);
+int prefill_tile_choice(int B, int H, int Sq, int Sk, int d, int dtype, int causal);
+int prefill16_tile_count(int d);
+bool prefill16_tile_info(int d, int tile, TileInfo* out);
+int prefill16_tile_choice(int B, int H, int Sq, int Sk, int d, int causal);
 
 // Split-over-keys forward: partial kernel + merge kernel.
 size_t splitk_workspace_bytes(int B, int H, int Sq, int d, int n_split);

@@ -65,7 +65,7 @@ def kernel_kind(kernel_name: str) -> str:
 def source_digest(kind: str) -> str:
     """sha256 over the sources of one kernel family (fused, splitk, naive)."""
     csrc = os.path.join(ROOT, "scaled_dot_product_flashattention_amd", "csrc")
-    files = {"fused": ["fwd_prefill.hip", "fwd_prefill16.hip", "device_common.h"],
+    files = {"fused": ["fwd_prefill.hip", "fwd_prefill16.hip", "tile_table.inc", "device_common.h"],
              "splitk": ["fwd_splitk.hip", "device_common.h"],
              "naive": ["naive.hip", "device_common.h"]}[kind]
     h = hashlib.sha256()

@@ -17,11 +17,15 @@ HEADER = os.path.join(ROOT, "include", "attn.h")
 
 OK, E_NULLPTR, E_SHAPE, E_UNSUPPORTED, E_ALIGN, E_WORKSPACE, E_HIP, E_ARG = range(8)
 BHSD, BSHD = 0, 1
+F32, F16, BF16 = 0, 1, 2
+
+
+N_TILES = {64: 4, 128: 4}  # tile variants of the 16-bit fused kernel per head size
 
 
 def SPLIT(g):  # heads in groups of g
     return 0x10000 | g
-F32, F16, BF16 = 0, 1, 2
+
 
 # fake, never dereferenced device addresses (validation fails before any use)
 A16 = 0x10000
@@ -190,3 +194,71 @@ def test_layout_names():
     assert layout_shape("split:4", 2, 8, 5, 64) == (2, 2, 5, 4, 64)
     with pytest.raises(ValueError):
         layout_code("bsdh")
+
+
+def test_tile_queries(lib):
+    """Variant counts and descriptions; every variant fits gfx950's 160 KiB
+    of LDS and 1024 threads per workgroup."""
+    for d in (64, 128):
+        assert lib.attn_fwd_tile_count(d, F32) == 1
+        for dt in (F16, BF16):
+            n = lib.attn_fwd_tile_count(d, dt)
+            assert n == N_TILES[d]
+            for t in range(n):
+                info = sdpa.attn_fwd_tile_info(d, {F16: torch.float16, BF16: torch.bfloat16}[dt], t)
+                assert info["rows"] % 128 == 0 and info["keys"] in (32, 64, 128)
+                assert info["waves"] in (4, 8) and 0 < info["lds_bytes"] <= 160 * 1024
+                assert info["stages"] >= 2
+    assert lib.attn_fwd_tile_count(96, BF16) == 0 and lib.attn_fwd_tile_count(64, 5) == 0
+    info = sdpa.api.TileInfo()
+    assert lib.attn_fwd_tile_info(64, BF16, 0, None) == E_NULLPTR
+    assert lib.attn_fwd_tile_info(96, BF16, 0, ctypes.byref(info)) == E_UNSUPPORTED
+    for bad in ((64, BF16, N_TILES[64]), (64, BF16, -1), (128, F32, 1), (128, BF16, N_TILES[128])):
+        assert lib.attn_fwd_tile_info(*bad, ctypes.byref(info)) == E_ARG, bad
+
+
+def test_tile_choice_covers_every_shape(lib):
+    """The compiled table gives a valid variant for every shape, including
+    the extremes of both grid axes (clamped), and fp32 has one variant."""
+    t = ctypes.c_int(-5)
+    for d in (64, 128):
+        for causal in (0, 1):
+            for B, H, Sq, Sk in ((1, 1, 1, 1), (1, 1, 1, 1 << 30), (1, 16, 4096, 4096),
+                                 (1 << 14, 1 << 15, 2, 3), (1, 1, 1 << 30, 7), (7, 3, 333, 5000)):
+                assert lib.attn_fwd_tile_choice(B, H, Sq, Sk, d, BF16, causal, ctypes.byref(t)) == OK
+                assert 0 <= t.value < N_TILES[d], (d, causal, B, H, Sq, Sk, t.value)
+                assert lib.attn_fwd_tile_choice(B, H, Sq, Sk, d, F32, causal, ctypes.byref(t)) == OK
+                assert t.value == 0
+    assert lib.attn_fwd_tile_choice(1, 1, 1, 1, 64, BF16, 0, None) == E_NULLPTR
+    assert lib.attn_fwd_tile_choice(0, 1, 1, 1, 64, BF16, 0, ctypes.byref(t)) == E_SHAPE
+
+
+def test_tile_table_entries():
+    """Every entry of the committed table names an existing variant."""
+    path = os.path.join(ROOT, "scaled_dot_product_flashattention_amd", "csrc", "tile_table.inc")
+    text = open(path).read()
+    body = text[text.index("kTileTable"):]
+    rows = re.findall(r"\{([0-9, ]+)\},", body)
+    consts = dict(re.findall(r"constexpr int (\w+) = (\d+);", text))
+    nr = int(consts["kTuneRowsBuckets"])
+    assert len(rows) == 2 * 2 * nr
+    for i, r in enumerate(rows):
+        vals = [int(x) for x in r.split(",")]
+        assert len(vals) == int(consts["kTuneKeysBuckets"])
+        d = 64 if i < 2 * nr else 128  # [head size][masking][rows]
+        assert all(0 <= x < N_TILES[d] for x in vals)
+
+
+def tiled(lib, tile=0, q=A16, k=A16, v=A16, o=A16_2, dtype=BF16, d=64, scale=0.125):
+    return lib.attn_fwd_tiled(q, k, v, o, None, 1, 2, 8, 8, d, scale, 0, BHSD, dtype, None, tile,
+                              None)
+
+
+def test_tiled_validation(lib):
+    for bad in (-2, N_TILES[64], 100):
+        assert tiled(lib, tile=bad) == E_ARG, bad
+    assert tiled(lib, tile=1, dtype=F32) == E_ARG
+    assert tiled(lib, q=None) == E_NULLPTR
+    assert tiled(lib, d=96) == E_UNSUPPORTED
+    assert tiled(lib, o=A16 + 8) == E_ALIGN
+    assert tiled(lib, scale=-1.0) == E_ARG
