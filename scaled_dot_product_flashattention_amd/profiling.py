@@ -54,20 +54,26 @@ def _pick(per_kernel: dict, needle: str):
 
 
 def kernel_kind(kernel_name: str) -> str:
-    """Which source family a kernel comes from: fused, splitk or naive."""
+    """Which source family a kernel comes from: fused, splitk, naive, qkv or softmax."""
     if "splitk" in kernel_name:
         return "splitk"
     if "naive" in kernel_name:
         return "naive"
+    if "qkv_proj" in kernel_name:
+        return "qkv"
+    if "softmax_" in kernel_name:
+        return "softmax"
     return "fused"
 
 
 def source_digest(kind: str) -> str:
-    """sha256 over the sources of one kernel family (fused, splitk, naive)."""
+    """sha256 over the sources of one kernel family (see kernel_kind)."""
     csrc = os.path.join(ROOT, "scaled_dot_product_flashattention_amd", "csrc")
     files = {"fused": ["fwd_prefill.hip", "fwd_prefill16.hip", "tile_table.inc", "device_common.h"],
              "splitk": ["fwd_splitk.hip", "device_common.h"],
-             "naive": ["naive.hip", "device_common.h"]}[kind]
+             "naive": ["naive.hip", "device_common.h"],
+             "qkv": ["qkv_proj.hip", "device_common.h"],
+             "softmax": ["softmax_rows.hip", "device_common.h"]}[kind]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(csrc, f)) as fh:
