@@ -14,13 +14,19 @@
 // product are contiguous along the contraction.
 //
 // Mapping to gfx950:
-//   * 128 x 128 output tile per workgroup, 4 waves of 64 x 64 (2 x 2 blocks
-//     of 32 x 32). The products are computed transposed, Y^T = W X^T, on
-//     32x32x16 matrix-core blocks: A = weight rows, B = token rows.
-//   * K steps of 64: the 128 x 64 tiles of X and W go global -> LDS by
-//     direct DMA loads into a two-stage ring (one tile ahead), rows of 128 B
-//     with their 16-byte chunks XOR-swizzled so the ds_read_b128 operand
-//     reads are free of bank conflicts.
+//   * 192 x 128 output tile per workgroup (192 weight rows = output columns,
+//     128 token rows), 4 waves of 96 x 64 (3 x 2 blocks of 32 x 32). The
+//     products are computed transposed, Y^T = W X^T, on 32x32x16 matrix-core
+//     blocks: A = weight rows, B = token rows. Each K-step of 16 reads 5
+//     operands from LDS for 6 products, which keeps LDS reads below what
+//     the LDS delivers at full matrix-core rate.
+//   * K steps of 64: the 128 x 64 tile of X and the 192 x 64 tile of W go
+//     global -> LDS by direct DMA loads into a two-stage ring (one tile
+//     ahead), rows of 128 B with their 16-byte chunks XOR-swizzled so the
+//     ds_read_b128 operand reads are free of bank conflicts. A stage is
+//     40 KiB, so two workgroups (8 waves) share a CU.
+//   * When the grid is a multiple of 8, consecutive tiles (token-row major)
+//     go to one XCD, so its L2 serves their shared X and W reads.
 //   * Epilogue: fp32 accumulators -> storage type (round to nearest even)
 //     -> LDS -> 16-byte stores, each chunk of 8 columns placed by (t, h, c).
 //   * Rows past M and columns past N reread the last valid row (finite) and
@@ -33,14 +39,18 @@ namespace attn {
 namespace {
 
 constexpr int QBM = 128;  // token rows per workgroup
-constexpr int QBN = 128;  // output columns per workgroup
+constexpr int QBN = 192;  // output columns (weight rows) per workgroup
 constexpr int QBK = 64;   // contraction per stage
 constexpr int QNT = 256;  // threads
+constexpr int QWN = 3;    // 32-column blocks per wave
+constexpr int QWM = 2;    // 32-row blocks per wave
 constexpr int QROW = QBK * 2;               // bytes per LDS row
-constexpr int QTILE = QBM * QROW;           // bytes of one 128 x 64 tile
-constexpr int QSTAGE = 2 * QTILE;           // X tile, then W tile
+constexpr int QXTILE = QBM * QROW;          // bytes of the X tile
+constexpr int QWTILE = QBN * QROW;          // bytes of the W tile
+constexpr int QSTAGE = QXTILE + QWTILE;     // X tile, then W tile
 constexpr int QNST = 2;
 constexpr int QOROW = QBN + 8;              // output staging row (elements)
+static_assert(QBM * QOROW * 2 <= QNST * QSTAGE, "output staging fits the ring");
 
 typedef __attribute__((address_space(3))) void lds_void_q;
 
@@ -52,6 +62,7 @@ struct QkvParams {
     int S, H, d;
     Strides so;    // output layout
     int n_ntiles;  // column tiles
+    int remap;     // grid size is a multiple of 8: contiguous tile ranges per XCD
 };
 
 template <int N> __device__ __forceinline__ void qwait_vmcnt() {
@@ -82,12 +93,15 @@ __global__ __launch_bounds__(QNT, 2) void qkv_proj_kernel(QkvParams p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1;  // 64-row half of the token rows
-    const int wn = wave & 1;   // 64-column half of the output columns
+    const int wn = wave & 1;   // 96-column half of the output columns
     const int n32 = lane & 31;
     const int hh = lane >> 5;
 
-    const int tm = blockIdx.x / p.n_ntiles;
-    const int tn = blockIdx.x - tm * p.n_ntiles;
+    const int G = gridDim.x;
+    const int g = blockIdx.x;
+    const int wg = p.remap ? (g & 7) * (G >> 3) + (g >> 3) : g;
+    const int tm = wg / p.n_ntiles;
+    const int tn = wg - tm * p.n_ntiles;
     const int m0 = tm * QBM, n0 = tn * QBN;
 
     const T* xp = static_cast<const T*>(p.x);
@@ -95,38 +109,43 @@ __global__ __launch_bounds__(QNT, 2) void qkv_proj_kernel(QkvParams p) {
 
     // DMA slots: thread-slot i*QNT + tid of a tile is chunk (row, pc) and
     // holds logical chunk pc ^ swz(row) of that row (rows clamped to valid).
-    constexpr int DMA1 = QTILE / 16 / QNT;  // 4 loads per thread and tile
-    int64_t xoff[DMA1], woff[DMA1];
+    constexpr int DMAX = QXTILE / 16 / QNT;  // 4 loads per thread for X
+    constexpr int DMAW = QWTILE / 16 / QNT;  // 6 loads per thread for W
+    static_assert(DMAX * 16 * QNT == QXTILE && DMAW * 16 * QNT == QWTILE, "tiles split over lanes");
+    int64_t xoff[DMAX], woff[DMAW];
 #pragma unroll
-    for (int i = 0; i < DMA1; ++i) {
+    for (int i = 0; i < DMAX; ++i) {
         const int slot = i * QNT + tid;
         const int row = slot / 8, pc = slot % 8;
-        const int xr = min(m0 + row, p.M - 1), wr = min(n0 + row, p.N - 1);
-        xoff[i] = (int64_t)xr * p.K + (pc ^ qswz(row)) * 8;
-        woff[i] = (int64_t)wr * p.K + (pc ^ qswz(row)) * 8;
+        xoff[i] = (int64_t)min(m0 + row, p.M - 1) * p.K + (pc ^ qswz(row)) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < DMAW; ++i) {
+        const int slot = i * QNT + tid;
+        const int row = slot / 8, pc = slot % 8;
+        woff[i] = (int64_t)min(n0 + row, p.N - 1) * p.K + (pc ^ qswz(row)) * 8;
     }
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_q*)smem;
     auto issue = [&](int kt) __attribute__((always_inline)) {
         const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + (kt % QNST) * QSTAGE + wave * 1024);
         const int64_t k0 = (int64_t)kt * QBK;
 #pragma unroll
-        for (int i = 0; i < DMA1; ++i) {
-            qdma16(xp + xoff[i] + k0, st + i * QNT * 16);
-            qdma16(wp + woff[i] + k0, st + i * QNT * 16 + QTILE);
-        }
+        for (int i = 0; i < DMAX; ++i) qdma16(xp + xoff[i] + k0, st + i * QNT * 16);
+#pragma unroll
+        for (int i = 0; i < DMAW; ++i) qdma16(wp + woff[i] + k0, st + QXTILE + i * QNT * 16);
     };
-    // operand of a 32-row block (rows rb*32.., K-step s) from a 128 x 64 tile
+    // operand of a 32-row block (rows rb*32.., K-step s) from a tile of 128-B rows
     auto operand = [&](const unsigned char* tile, int rb, int s) __attribute__((always_inline)) -> u32x4 {
         const int row = rb * 32 + n32;
         const int lc = 2 * s + hh;
         return *reinterpret_cast<const u32x4*>(tile + row * QROW + ((lc ^ qswz(row)) << 4));
     };
 
-    f32x16 acc[2][2];  // [n block][m block] of Y^T
+    f32x16 acc[QWN][QWM];  // [n block][m block] of Y^T
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < QWN; ++a)
 #pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2)
+        for (int b2 = 0; b2 < QWM; ++b2)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b2][r] = 0.f;
 
@@ -137,37 +156,36 @@ __global__ __launch_bounds__(QNT, 2) void qkv_proj_kernel(QkvParams p) {
         qbarrier();         // everyone's part; everyone is done with tile kt-1
         if (kt + 1 < nk) issue(kt + 1);
         const unsigned char* xt = smem + (kt % QNST) * QSTAGE;
-        const unsigned char* wt = xt + QTILE;
+        const unsigned char* wt = xt + QXTILE;
 #pragma unroll
         for (int s = 0; s < QBK / 16; ++s) {
-            u32x4 wa[2], xb[2];
+            u32x4 wa[QWN], xb[QWM];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                wa[j] = operand(wt, wn * 2 + j, s);
-                xb[j] = operand(xt, wm * 2 + j, s);
-            }
+            for (int j = 0; j < QWN; ++j) wa[j] = operand(wt, wn * QWN + j, s);
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int j = 0; j < QWM; ++j) xb[j] = operand(xt, wm * QWM + j, s);
 #pragma unroll
-                for (int b2 = 0; b2 < 2; ++b2) acc[a][b2] = mfma16<Tag>(wa[a], xb[b2], acc[a][b2]);
+            for (int a = 0; a < QWN; ++a)
+#pragma unroll
+                for (int b2 = 0; b2 < QWM; ++b2) acc[a][b2] = mfma16<Tag>(wa[a], xb[b2], acc[a][b2]);
         }
     }
     __syncthreads();  // all DMA landed and all operand reads done
 
     // ---- epilogue: Y tile (rows m, columns n) in LDS, then 16-byte stores ---
-    // acc[a][b2] register r of lane (n32, hh): column n = (wn*2+a)*32 +
-    // blk_row(r, hh) of the tile, row m = (wm*2+b2)*32 + n32.
+    // acc[a][b2] register r of lane (n32, hh): column n = (wn*QWN+a)*32 +
+    // blk_row(r, hh) of the tile, row m = (wm*QWM+b2)*32 + n32.
     T* Ys = reinterpret_cast<T*>(smem);
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < QWN; ++a)
 #pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2) {
-            const int row = (wm * 2 + b2) * 32 + n32;
+        for (int b2 = 0; b2 < QWM; ++b2) {
+            const int row = (wm * QWM + b2) * 32 + n32;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int col = (wn * 2 + a) * 32 + 8 * g + 4 * hh;
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int col = (wn * QWN + a) * 32 + 8 * g4 + 4 * hh;
                 const f32x16& v = acc[a][b2];
-                const u32x2 pk = {pack2<Tag>(v[4 * g], v[4 * g + 1]), pack2<Tag>(v[4 * g + 2], v[4 * g + 3])};
+                const u32x2 pk = {pack2<Tag>(v[4 * g4], v[4 * g4 + 1]), pack2<Tag>(v[4 * g4 + 2], v[4 * g4 + 3])};
                 *reinterpret_cast<u32x2*>(Ys + row * QOROW + col) = pk;
             }
         }
@@ -205,6 +223,7 @@ hipError_t run_qkv_proj(const QkvArgs& a, hipStream_t stream) {
     p.n_ntiles = (p.N + QBN - 1) / QBN;
     const int64_t grid = (int64_t)((p.M + QBM - 1) / QBM) * p.n_ntiles;
     if (grid > 0x7fffffff || grid == 0) return grid == 0 ? hipSuccess : hipErrorInvalidValue;
+    p.remap = (grid % 8 == 0) ? 1 : 0;
     if (a.dtype == 2)
         hipLaunchKernelGGL(qkv_proj_kernel<BF16>, dim3((unsigned)grid), dim3(QNT), 0, stream, p);
     else
