@@ -19,23 +19,31 @@ W = WORKLOADS
 N_TILES = {64: 4, 128: 4}  # variants per head size (the ABI tests check the library agrees)
 CASES = [(dt, d, t) for dt, d in (("bf16", 64), ("f16", 64), ("bf16", 128), ("f16", 128))
          for t in range(N_TILES[d])]
-SHAPES = {  # name: (B, H, Sq, Sk, causal, kv_len range, layout)
-    "single_tile": (1, 1, 40, 70, False, None, "bhsd"),
-    "ragged": (2, 3, 300, 700, False, (200, 700), "bhsd"),
-    "causal_square": (1, 2, 520, 520, True, None, "bshd"),
-    "causal_more_queries": (2, 2, 300, 100, True, (0, 100), "bhsd"),
-    "split_groups": (2, 4, 260, 2100, True, (1000, 2100), "split:2"),
+SHAPES = {  # name: (B, H, Sq, Sk, causal, kv_len range, layout, extra workload fields)
+    "single_tile": (1, 1, 40, 70, False, None, "bhsd", {}),
+    "ragged": (2, 3, 300, 700, False, (200, 700), "bhsd", {}),
+    "causal_square": (1, 2, 520, 520, True, None, "bshd", {}),
+    "causal_more_queries": (2, 2, 300, 100, True, (0, 100), "bhsd", {}),
+    "split_groups": (2, 4, 260, 2100, True, (1000, 2100), "split:2", {}),
+    # q, k x 4: the sums leave range, the reference max moves between tiles
+    "large_scores": (1, 2, 400, 900, True, (500, 900), "bhsd", {"qk_mult": 4.0}),
+    # scale * log2(e) > 1: queries are not pre-scaled
+    "scale_above_one": (1, 2, 300, 700, False, None, "bhsd", {"scale": 2.0}),
+    # the largest scale that still pre-scales, on large scores
+    "scale_at_one": (1, 2, 300, 700, False, None, "bhsd", {"scale": 0.69, "qk_mult": 2.0}),
 }
 
 
 @pytest.mark.parametrize("shape", list(SHAPES))
 @pytest.mark.parametrize("dtype,d,tile", CASES)
 def test_tile_variant_matches_oracle(dtype, d, tile, shape):
-    B, H, Sq, Sk, causal, pad, layout = SHAPES[shape]
+    B, H, Sq, Sk, causal, pad, layout, extra = SHAPES[shape]
+    extra = dict(extra)
+    scale = extra.pop("scale", None)
     w = W["medium_bf16"].replace(name=f"{shape}_t{tile}", B=B, H=H, Sq=Sq, Sk=Sk, d=d, dtype=dtype,
                                  causal=causal, kv_len_range=pad, layout=layout,
-                                 seed=70 + tile + d)
-    full_case(w, path=f"tile:{tile}", poison=pad is not None)
+                                 seed=70 + tile + d, **extra)
+    full_case(w, path=f"tile:{tile}", poison=pad is not None, scale=scale)
 
 
 @pytest.mark.parametrize("name,tile", [(n, t) for n in ("medium_bf16", "long_causal_bf16", "bert_pad_fp16")
