@@ -64,6 +64,17 @@ def cpu_share() -> int:
     return max(1, min(16, n))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, t, target_s: float = 12.0):
     """The fp64 oracle on a bounded sample of rows of the same workload,
     timed on the host cores, scaled to the metric's unit."""
@@ -90,6 +101,7 @@ def cpu_baseline(w, t, target_s: float = 12.0):
     else:
         f = 4.0 * w.d * w.Sk * len(rows)
     return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{len(rows)} of {R} query rows of the same workload, full key range each, "
                       f"{dt:.1f} s wall on {cores} threads (fp64, three-step softmax)"}
 
