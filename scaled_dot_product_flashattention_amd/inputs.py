@@ -101,6 +101,30 @@ def generate(w: Workload, seed: int | None = None) -> dict:
     return out
 
 
+def generate_periodic_keys(w: Workload, period: int, seed: int | None = None) -> dict:
+    """Like ``generate`` but K and V repeat a random block of ``period`` key
+    rows along the sequence (key j is block row j mod period), so very long
+    key ranges cost one block of random draws. q is drawn in full. A prime
+    period keeps any offset error of a power-of-two size from landing on an
+    identical key. [B,S,H,d] layout only."""
+    if w.layout != "bshd":
+        raise ValueError("periodic keys are drawn for the [B,S,H,d] layout")
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    tdt = DTYPES[w.dtype]
+    out = {"q": torch.from_numpy(rng.standard_normal(w.shape(w.Sq), dtype=np.float32)).to(tdt)}
+    reps = -(-w.Sk // period)
+    for name in ("k", "v"):
+        block = torch.from_numpy(rng.standard_normal((w.B, period, w.H, w.d), dtype=np.float32)).to(tdt)
+        out[name] = block.repeat(1, reps, 1, 1)[:, :w.Sk].contiguous()
+        del block
+    if w.kv_len_range is not None:
+        lo, hi = w.kv_len_range
+        out["kv_len"] = torch.from_numpy(rng.integers(lo, hi + 1, size=w.B).astype(np.int32))
+    else:
+        out["kv_len"] = None
+    return out
+
+
 def generate_qkv_proj(B: int, S: int, D: int, H: int, d: int, dtype: str, seed: int) -> dict:
     """Tokens x [B, S, D] ~ N(0, 1) and an out-major weight w [3*H*d, D] ~
     N(0, 1/D) (a standard linear-layer initialisation: outputs of unit scale),
