@@ -64,6 +64,31 @@ def cpu_share() -> int:
     return max(1, min(16, n))
 
 
+def timed_region(step, steps: int, stream, torch):
+    """Run ``steps`` calls of ``step`` on ``stream`` between HIP events, in
+    five equal batches (the last takes the remainder) with an event at each
+    boundary. Returns the mean ms per step over the whole region and the
+    per-step means of the batches."""
+    nb = min(5, steps)
+    sizes = [steps // nb + (1 if i < steps % nb else 0) for i in range(nb)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+    ev[0].record(stream)
+    for i, n in enumerate(sizes):
+        for _ in range(n):
+            step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    total = ev[0].elapsed_time(ev[nb]) / steps
+    batches = [ev[i].elapsed_time(ev[i + 1]) / sizes[i] for i in range(nb)]
+    return total, batches
+
+
+def timing_summary(ms: float, batches) -> dict:
+    srt = sorted(batches)
+    return {"ms_mean": round(ms, 5), "ms_median_of_batches": round(srt[len(srt) // 2], 5),
+            "ms_min_of_batches": round(srt[0], 5), "batches": len(batches)}
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -122,14 +147,7 @@ def bench_softmax(args, w, torch, sdpa) -> int:
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, batches = timed_region(step, args.steps, stream, torch)
     es = x.element_size()
     nbytes = float(rows) * n * 2 * es + rows * 4  # x read once, y written once, lse
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -140,6 +158,7 @@ def bench_softmax(args, w, torch, sdpa) -> int:
         "scaling": "weak", "vs_baseline": None,
         "dtype": {"f32": "f32", "f16": "fp16", "bf16": "bf16"}[w.dtype], "data": "synthetic",
         "config": {"workload": w.name, "rows": rows, "n": n, "path": args.path},
+        "timing": timing_summary(ms, batches),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel_ms": round(ms, 5),
                      "algorithmic_units": "bytes per launch (x once, y once, lse)",
@@ -191,14 +210,7 @@ def bench_qkv(args, w, torch, sdpa) -> int:
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, batches = timed_region(step, args.steps, stream, torch)
     tflops = fl / (ms * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS_16, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_TFLOPS_16, 4), "traffic": None, "kernel_ms": round(ms, 5),
@@ -213,6 +225,7 @@ def bench_qkv(args, w, torch, sdpa) -> int:
         "dtype": {"f16": "fp16", "bf16": "bf16"}[w.dtype], "data": "synthetic",
         "config": {"workload": w.name, "B": B, "S": S, "D": D, "H": H, "d": d, "layout": w.layout,
                    "causal": w.causal, "path": args.path, "flops_per_step": fl},
+        "timing": timing_summary(ms, batches),
         "roofline": roof,
     }
     print(json.dumps(line), flush=True)
@@ -297,16 +310,9 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
+    ms, batches = timed_region(step, args.steps, stream, torch)
     wall_ms = (time.perf_counter() - t_wall) * 1e3
-    ms = e0.elapsed_time(e1) / args.steps
 
     peak_bytes = torch.cuda.max_memory_allocated(dev)
     if args.copy_calibration:
@@ -357,6 +363,7 @@ def main() -> int:
                    "Sk": Sk, "d": d, "layout": w.layout, "causal": w.causal, "path": args.path,
                    "n_split": n_split, "tile": tile, "flops_per_step": fl, "wall_ms_timed_region": round(wall_ms, 2),
                    "peak_device_bytes": peak_bytes},
+        "timing": timing_summary(ms, batches),
         "roofline": roof,
     }
     if not args.skip_cpu_baseline:

@@ -7,9 +7,10 @@
 // the online one, where a running maximum and a running sum rescaled by
 // exp(m_old - m_new) come out of a single pass (chapter "2. 自注意力机制算子…",
 // §2.3 and §2.6). Both are here:
-//   * online: the threads of a row (64 to 1024, as few as hold it; short
-//     rows share a workgroup) keep the row in registers, 32 values each, up
-//     to 32768 per row, so each element is read once and written once; with
+//   * online: the threads of a row (64 to 1024, as few as hold it; rows of
+//     at most 1024 values go 2 or 4 to a wave, with all their loads issued
+//     together) keep the row in registers, 32 values each, up to 32768 per
+//     row, so each element is read once and written once; with
 //     the values on chip, the row max and then the row sum are plain
 //     reductions. Longer rows stream twice: a pass of per-thread online
 //     (m, l) updates over 16-byte chunks, the threads' pairs merged with
@@ -229,6 +230,76 @@ __global__ __launch_bounds__(threads_of<TPR>()) void softmax_online_kernel(Softm
     if (live && tid == 0 && p.lse != nullptr) p.lse[row] = l > 0.f ? (m + log2f(l)) * kLn2 : kNegInfS;
 }
 
+// Short rows (at most 64 * SVALS / RPW values): each wave holds RPW rows,
+// one after another, issuing all their loads before any reduction, so that
+// a wave keeps RPW times more bytes in flight; each row reduces across the
+// wave's 64 lanes only (no barriers).
+template <typename Tag, int RPW>
+__global__ __launch_bounds__(256) void softmax_online_short_kernel(SoftmaxParams p) {
+    using C = Chunk<Tag>;
+    constexpr int E = C::E;
+    constexpr int EB = 16;
+    constexpr int SPR = SVALS / E / RPW;  // chunk slots per lane and row
+    static_assert(SPR >= 1, "rows per wave exceed the register slots");
+    const int lane = threadIdx.x & 63;
+    const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW;
+    const int nch = p.n / E;
+    float v[RPW][SPR][E];
+    float m[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        const bool live = row0 + r < p.rows;
+        const unsigned char* xr = static_cast<const unsigned char*>(p.x) + (row0 + r) * (int64_t)p.n * (EB / E);
+        m[r] = kNegInfS;
+#pragma unroll
+        for (int j = 0; j < SPR; ++j) {
+            const int ci = lane + j * 64;
+            if (live && ci < nch) {
+                C::load(xr + (int64_t)ci * EB, v[r][j]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) v[r][j][e] = kNegInfS;
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+#pragma unroll
+        for (int j = 0; j < SPR; ++j)
+#pragma unroll
+            for (int e = 0; e < E; ++e) { v[r][j][e] *= p.c; m[r] = fmaxf(m[r], v[r][j][e]); }
+        m[r] = RowReduce<64>::max(m[r], nullptr);
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        const bool live = row0 + r < p.rows;
+        float l = 0.f;
+        if (m[r] != kNegInfS) {
+#pragma unroll
+            for (int j = 0; j < SPR; ++j)
+                if (lane + j * 64 < nch) {  // slots past the row hold nothing
+#pragma unroll
+                    for (int e = 0; e < E; ++e) l += fast_exp2(v[r][j][e] - m[r]);
+                }
+        }
+        l = RowReduce<64>::sum(l, nullptr);
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const float mu = m[r] == kNegInfS ? 0.f : m[r];
+        unsigned char* yr = static_cast<unsigned char*>(p.y) + (row0 + r) * (int64_t)p.n * (EB / E);
+#pragma unroll
+        for (int j = 0; j < SPR; ++j) {
+            const int ci = lane + j * 64;
+            if (live && ci < nch) {
+                float o[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) o[e] = fast_exp2(v[r][j][e] - mu) * inv;
+                C::store(yr + (int64_t)ci * EB, o);
+            }
+        }
+        if (live && lane == 0 && p.lse != nullptr) p.lse[row0 + r] = l > 0.f ? (m[r] + log2f(l)) * kLn2 : kNegInfS;
+    }
+}
+
 template <typename Tag, int TPR>
 __global__ __launch_bounds__(threads_of<TPR>()) void softmax_three_pass_kernel(SoftmaxParams p) {
     using C = Chunk<Tag>;
@@ -300,6 +371,16 @@ hipError_t launch_softmax(const SoftmaxArgs& a, hipStream_t stream) {
     p.c = a.scale > 0.f ? a.scale * kLog2e : 1e-30f;
     const int per_thread = SVALS;  // values per thread in registers
     const int64_t need = (a.n + per_thread - 1) / per_thread;
+    if (a.mode == 0 && need <= 32) {
+        // short rows: several per wave (4 waves, 4 * RPW rows per workgroup)
+        const int rpw = need <= 16 ? 4 : 2;
+        const int64_t grid = (p.rows + 4 * rpw - 1) / (4 * rpw);
+        if (rpw == 4)
+            hipLaunchKernelGGL((softmax_online_short_kernel<Tag, 4>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((softmax_online_short_kernel<Tag, 2>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+        return hipGetLastError();
+    }
     if (need <= 64) return launch_softmax_tpr<Tag, 64>(p, a.mode, stream);
     if (need <= 128) return launch_softmax_tpr<Tag, 128>(p, a.mode, stream);
     if (need <= 256) return launch_softmax_tpr<Tag, 256>(p, a.mode, stream);

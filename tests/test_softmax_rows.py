@@ -39,6 +39,8 @@ def check(y, lse, y_ref, lse_ref, dtype, what):
 
 CASES = [  # rows, n: a chunk, a few, one full register load, the most, streamed
     (3, 8), (5, 64), (7, 1000 - 1000 % 8), (4, 4096), (3, 32768), (2, 40000), (2, 65536),
+    # the edges of 4 rows per wave (<= 512), 2 rows per wave (<= 1024) and one
+    (37, 512), (37, 520), (19, 1024), (19, 1032),
 ]
 
 
@@ -71,7 +73,22 @@ def test_softmax_rows_masked_and_scale_zero(mode):
         check(y, lse, y_ref, lse_ref, "bf16", f"{mode} masked scale {scale}")
 
 
-@pytest.mark.parametrize("n", [4096, 32768, 65536])
+@pytest.mark.parametrize("mode", ["online", "three_pass"])
+@pytest.mark.parametrize("n", [512, 1024])
+def test_short_rows_masked(mode, n):
+    """Rows held several to a wave: masked entries, an all -inf row between
+    live ones, and a row count that leaves the last wave partly empty."""
+    x = generate_softmax_rows(23, n, "bf16", seed=n + 3)
+    x[0, 100:] = float("-inf")
+    x[5, :] = float("-inf")
+    x[6, ::3] = float("-inf")
+    y_ref, lse_ref = oracle.softmax_rows(x, scale=0.9)
+    y, lse = sdpa.attn_softmax_rows(x.cuda(), scale=0.9, mode=mode)
+    torch.cuda.synchronize()
+    check(y, lse, y_ref, lse_ref, "bf16", f"{mode} short masked n{n}")
+
+
+@pytest.mark.parametrize("n", [512, 1024, 4096, 32768, 65536])
 def test_online_equals_three_pass(n):
     """The page's guard: both forms agree within 1e-3 (here much closer)."""
     x = generate_softmax_rows(16, n, "f32", seed=n, std=4.0).cuda()
