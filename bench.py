@@ -247,6 +247,11 @@ def main() -> int:
                          "copies, then attention), or the row softmax (online or "
                          "three-pass) over the workload's B*H*Sq score rows of Sk")
     ap.add_argument("--n-split", type=int, default=None)
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time graph replays (fused and "
+                         "splitk paths)")
+    ap.add_argument("--shape", default=None,
+                    help="override the workload's B,H,Sq,Sk (e.g. 1,8,1,4096 for a small decode)")
     ap.add_argument("--layout", default=None,
                     help="override the workload's tensor layout: bhsd ([B,H,S,d]), bshd "
                          "([B,S,H,d]) or split:g ([B,H/g,S,g,d], heads in groups of g)")
@@ -274,6 +279,12 @@ def main() -> int:
     relaid = args.layout is not None and args.layout != w.layout
     if relaid:
         w = w.replace(layout=args.layout)
+    if args.shape:
+        B_, H_, Sq_, Sk_ = (int(x) for x in args.shape.split(","))
+        kv = None if w.kv_len_range is None else (min(w.kv_len_range[0], Sk_), Sk_)
+        w = w.replace(B=B_, H=H_, Sq=Sq_, Sk=Sk_, kv_len_range=kv,
+                      description=f"{w.name} at B{B_} H{H_} Sq{Sq_} Sk{Sk_}")
+        relaid = True  # not the study's shape: no headline metric, no stored traffic
     if args.path.startswith("qkv"):
         return bench_qkv(args, w, torch, sdpa)
     if args.path.startswith("softmax"):
@@ -309,6 +320,18 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.graph:
+        if args.path == "naive":
+            print("--graph covers the fused and splitk paths", file=sys.stderr)
+            return 2
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        step = g.replay
+        for _ in range(min(args.warmup, 50)):
+            step()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     t_wall = time.perf_counter()
     ms, batches = timed_region(step, args.steps, stream, torch)
@@ -361,6 +384,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "B": B, "H": H, "Sq": Sq,
                    "Sk": Sk, "d": d, "layout": w.layout, "causal": w.causal, "path": args.path,
+                   "graph": args.graph,
                    "n_split": n_split, "tile": tile, "flops_per_step": fl, "wall_ms_timed_region": round(wall_ms, 2),
                    "peak_device_bytes": peak_bytes},
         "timing": timing_summary(ms, batches),
