@@ -176,12 +176,27 @@ def dims(q: torch.Tensor, k: torch.Tensor, layout: str):
     return int(B), int(H), int(Sq), int(Sk), int(d)
 
 
+def _check_buffer(name, t, device, shape=None, dtype=None):
+    """A caller-supplied buffer: on `device`, dense, and of the stated shape
+    and dtype; anything else would hand the kernels a wrong address or size."""
+    if not isinstance(t, torch.Tensor) or t.device != device:
+        raise ValueError(f"{name} must be a tensor on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+
+
 def _prepare(q, k, v, layout, kv_len, scale, lse, return_lse, out):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
             raise ValueError(f"{name} must be a CUDA (HIP) tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous in the {layout} layout")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on one device")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share one dtype")
     if q.dim() != k.dim() or tuple(k.shape) != tuple(v.shape):
@@ -197,10 +212,11 @@ def _prepare(q, k, v, layout, kv_len, scale, lse, return_lse, out):
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q) if out is None else out
-    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
-        raise ValueError("out must match q in shape, dtype and layout")
+    _check_buffer("out", o, q.device, q.shape, q.dtype)
     if lse is None and return_lse:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check_buffer("lse", lse, q.device, (B, H, Sq), torch.float32)
     return (B, H, Sq, Sk, d), kv_len, float(scale), o, lse
 
 
@@ -215,10 +231,11 @@ def _stream(q, stream):
 
 
 def _scratch(nbytes, device, given):
+    if given is not None:
+        _check_buffer("workspace", given, device)
+        return given
     if nbytes == 0:
         return None
-    if given is not None:
-        return given
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
@@ -303,11 +320,14 @@ def attn_qkv_proj(x, w, *, H, d, layout="bhsd", out=None, stream=None):
     if tuple(w.shape) != (3 * H * d, D):
         raise ValueError(f"w has shape {tuple(w.shape)}, expected {(3 * H * d, D)}")
     shape = layout_shape(layout, B, int(H), S, int(d))
+    if x.device != w.device:
+        raise ValueError("x and w must be on one device")
     if out is None:
         out = tuple(torch.empty(shape, dtype=x.dtype, device=x.device) for _ in range(3))
-    for t in out:
-        if tuple(t.shape) != shape or t.dtype != x.dtype or not t.is_contiguous():
-            raise ValueError("out tensors must be dense, of x's dtype and shape " + str(shape))
+    if len(out) != 3:
+        raise ValueError("out must hold three tensors (q, k, v)")
+    for name, t in zip(("out q", "out k", "out v"), out):
+        _check_buffer(name, t, x.device, shape, x.dtype)
     rc = load_library().attn_qkv_proj(_ptr(x), _ptr(w), *(_ptr(t) for t in out), B, S, D, int(H),
                                       int(d), layout_code(layout), dtype_code(x.dtype),
                                       _stream(x, stream))
@@ -328,12 +348,15 @@ def attn_softmax_rows(x, *, scale=1.0, mode="online", return_lse=True, out=None,
         raise ValueError("x must be a 2-D CUDA (HIP) tensor")
     if not x.is_contiguous():
         raise ValueError("x must be contiguous")
+    if mode not in _SOFTMAX_MODES:
+        raise ValueError(f"mode must be 'online' or 'three_pass', not {mode!r}")
     rows, n = (int(a) for a in x.shape)
     y = torch.empty_like(x) if out is None else out
-    if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
-        raise ValueError("out must match x in shape and dtype")
+    _check_buffer("out", y, x.device, x.shape, x.dtype)
     if lse is None and return_lse:
         lse = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    elif lse is not None:
+        _check_buffer("lse", lse, x.device, (rows,), torch.float32)
     rc = load_library().attn_softmax_rows(_ptr(x), _ptr(y), _ptr(lse), rows, n, float(scale),
                                           dtype_code(x.dtype), _SOFTMAX_MODES[mode],
                                           _stream(x, stream))

@@ -262,3 +262,19 @@ def test_tiled_validation(lib):
     assert tiled(lib, d=96) == E_UNSUPPORTED
     assert tiled(lib, o=A16 + 8) == E_ALIGN
     assert tiled(lib, scale=-1.0) == E_ARG
+
+
+def test_binding_buffer_checks():
+    """Caller-supplied buffers must sit on the inputs' device, be dense and
+    have the stated shape and dtype (host-only check, before any launch)."""
+    from scaled_dot_product_flashattention_amd.api import _check_buffer
+    cpu, gpu = torch.device("cpu"), torch.device("cuda:0")
+    good = torch.zeros(2, 3, 4, dtype=torch.float32)
+    _check_buffer("lse", good, cpu, (2, 3, 4), torch.float32)
+    for args in ((good, gpu, (2, 3, 4), torch.float32),          # wrong device
+                 (good, cpu, (2, 3, 5), torch.float32),          # wrong shape
+                 (good, cpu, (2, 3, 4), torch.bfloat16),         # wrong dtype
+                 (good.transpose(0, 2), cpu, None, None),        # not dense
+                 (None, cpu, None, None)):                        # not a tensor
+        with pytest.raises(ValueError):
+            _check_buffer("x", *args)

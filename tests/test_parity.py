@@ -126,3 +126,25 @@ def test_split_layout_full_size_sampled():
     """Medium prefill shape (B1 H16 S4096 d64 bf16) in groups of 4 heads, at
     full size, on sampled rows."""
     sampled_case(W["medium_bf16"].replace(name="medium_split4", layout="split:4"))
+
+
+def test_binding_rejects_bad_buffers():
+    """Host-side rejection of buffers that would send a kernel a wrong address
+    or size: nothing is launched for any of these calls."""
+    import scaled_dot_product_flashattention_amd as sdpa
+    from scaled_dot_product_flashattention_amd.inputs import generate
+    w = W["medium_bf16"].replace(H=2, Sq=64, Sk=64)
+    t = generate(w)
+    q, k, v = (t[n].cuda() for n in ("q", "k", "v"))
+    bad = [dict(lse=torch.empty(1, 2, 64)),                                  # host LSE
+           dict(lse=torch.empty(1, 2, 63, device="cuda")),                   # short LSE
+           dict(lse=torch.empty(1, 2, 64, device="cuda", dtype=torch.float16)),
+           dict(out=torch.empty_like(q).cpu()),                              # host output
+           dict(workspace=torch.empty(1 << 20, dtype=torch.uint8))]          # host workspace
+    for kw in bad:
+        with pytest.raises(ValueError):
+            sdpa.attn_fwd(q, k, v, **kw)
+    with pytest.raises(ValueError):
+        sdpa.attn_softmax_rows(q.view(-1, 64), lse=torch.empty(5, device="cuda"))
+    with pytest.raises(ValueError):
+        sdpa.attn_softmax_rows(q.view(-1, 64), mode="two_pass")
