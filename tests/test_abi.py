@@ -278,3 +278,23 @@ def test_binding_buffer_checks():
                  (None, cpu, None, None)):                        # not a tensor
         with pytest.raises(ValueError):
             _check_buffer("x", *args)
+
+
+def test_header_is_c(tmp_path):
+    """include/attn.h is plain C: a C99 translation unit that includes it and
+    takes the address of every declared function compiles without warnings."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    names = declared_functions()
+    src = tmp_path / "use_attn.c"
+    src.write_text('#include "attn.h"\n#include <stddef.h>\ntypedef void (*any_fn)(void);\n'
+                   'int main(void) {\n'
+                   + "".join(f"    any_fn p_{n} = (any_fn)&{n}; (void)p_{n};\n" for n in names)
+                   + "    return ATTN_OK + ATTN_LAYOUT_SPLIT(2) * 0;\n}\n")
+    res = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", f"-I{ROOT}/include",
+                          "-c", str(src), "-o", str(tmp_path / "use_attn.o")],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
