@@ -93,7 +93,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * Returns 0 for arguments attn_fwd would reject. Host only. */
 size_t attn_fwd_workspace_size(int B, int H, int Sq, int Sk, int d, int dtype);
 
-/* The number of key splits attn_fwd will use (1 = single fused kernel).
+/* The number of key splits attn_fwd will use (1 = single fused kernel; at
+ * most 4 queries per head over at least 1024 keys always split).
  * Host only; returns a status and writes *n_split on success. */
 int attn_fwd_plan(int B, int H, int Sq, int Sk, int d, int dtype, int* n_split);
 

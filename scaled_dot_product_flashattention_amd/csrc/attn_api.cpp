@@ -15,10 +15,16 @@
 namespace {
 
 constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
-constexpr int kPrefillRowsPerWorkgroup = 128;
-constexpr int kSplitMaxQueries = 4;     // query rows at which the split path can pay off
-constexpr int kSplitTargetGroups = 2048; // about 8 workgroups per compute unit
-constexpr int kSplitMinKeys = 512;      // keys per split, at least
+// Split plan for few queries over many keys (measured on MI355X over
+// decode shapes of 8 to 1024 query rows and 4096 to 131072 keys): the
+// split kernels beat the fused kernel whenever each head has at most 4
+// queries (its 128-query tiles would be mostly empty), and they run best
+// with about 2 workgroups per compute unit and at most about 4096 keys per
+// split.
+constexpr int kSplitMaxQueries = 4;      // query rows per head at which the split path is used
+constexpr int kSplitTargetGroups = 512;  // about 2 workgroups per compute unit
+constexpr int kSplitMaxKeys = 4096;      // keys per split, at most (more splits past that)
+constexpr int kSplitMinKeys = 512;       // keys per split, at least
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -56,14 +62,15 @@ int check_call(const void* q, const void* k, const void* v, const void* o, const
 
 int plan_splits(int B, int H, int Sq, int Sk) {
     if (Sq > kSplitMaxQueries) return 1;
-    const int64_t prefill_groups = (int64_t)((Sq + kPrefillRowsPerWorkgroup - 1) / kPrefillRowsPerWorkgroup) * B * H;
-    if (prefill_groups >= kSplitTargetGroups / 4) return 1;
     const int64_t rows = (int64_t)B * H * Sq;
     int64_t n = (kSplitTargetGroups + rows - 1) / rows;
-    const int64_t max_by_keys = Sk / kSplitMinKeys;
-    if (n > max_by_keys) n = max_by_keys;
+    if (n < Sk / kSplitMaxKeys) n = Sk / kSplitMaxKeys;
+    if (n > Sk / kSplitMinKeys) n = Sk / kSplitMinKeys;
     if (n > 256) n = 256;
-    return n < 2 ? 1 : (int)n;
+    // even at one split per row the split kernels beat the fused kernel
+    // here; only very short key ranges stay fused (one launch)
+    if (n < 2) return Sk >= 2 * kSplitMinKeys ? 2 : 1;
+    return (int)n;
 }
 
 attn::FwdArgs make_args(const void* q, const void* k, const void* v, void* o, float* lse,
