@@ -123,8 +123,10 @@ __global__ __launch_bounds__(256) void splitk_partial_kernel(SplitParams p) {
         for (int u = 0; u < C::U; ++u) {
             jj[u] = j0 + (u * C::NW + wave) * C::KPW + grp;
             const u32x4 z = {0u, 0u, 0u, 0u};
-            kr[u] = jj[u] < ke ? *reinterpret_cast<const u32x4*>(kb + (int64_t)jj[u] * p.sk.s) : z;
-            vr[u] = jj[u] < ke ? *reinterpret_cast<const u32x4*>(vb + (int64_t)jj[u] * p.sk.s) : z;
+            // K and V are read exactly once: non-temporal loads keep them
+            // out of the caches (measured 6.0 -> 6.8 TB/s at B8 H32 Sk32768)
+            kr[u] = jj[u] < ke ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (int64_t)jj[u] * p.sk.s)) : z;
+            vr[u] = jj[u] < ke ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + (int64_t)jj[u] * p.sk.s)) : z;
         }
         float x[C::U];
 #pragma unroll

@@ -40,45 +40,54 @@ struct SoftmaxParams {
     float c;  // scale * log2(e), > 0
 };
 
-// 16-byte chunk <-> fp32 values
+// 16-byte chunk <-> fp32 values. NT: a non-temporal access, for data touched
+// for the last time (the online kernels read x once and write y once; the
+// three-pass kernel re-reads x and keeps it cached).
 template <typename Tag> struct Chunk;
 template <> struct Chunk<BF16> {
     static constexpr int E = 8;
-    __device__ static void load(const void* p, float (&v)[E]) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+    template <bool NT = false> __device__ static void load(const void* p, float (&v)[E]) {
+        const u32x4* a = reinterpret_cast<const u32x4*>(p);
+        const u32x4 w = NT ? __builtin_nontemporal_load(a) : *a;
 #pragma unroll
         for (int i = 0; i < 4; ++i) { v[2 * i] = lo16<BF16>(w[i]); v[2 * i + 1] = hi16<BF16>(w[i]); }
     }
-    __device__ static void store(void* p, const float (&v)[E]) {
+    template <bool NT = false> __device__ static void store(void* p, const float (&v)[E]) {
         u32x4 w;
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = pack2<BF16>(v[2 * i], v[2 * i + 1]);
-        *reinterpret_cast<u32x4*>(p) = w;
+        u32x4* a = reinterpret_cast<u32x4*>(p);
+        if (NT) __builtin_nontemporal_store(w, a); else *a = w;
     }
 };
 template <> struct Chunk<F16> {
     static constexpr int E = 8;
-    __device__ static void load(const void* p, float (&v)[E]) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+    template <bool NT = false> __device__ static void load(const void* p, float (&v)[E]) {
+        const u32x4* a = reinterpret_cast<const u32x4*>(p);
+        const u32x4 w = NT ? __builtin_nontemporal_load(a) : *a;
 #pragma unroll
         for (int i = 0; i < 4; ++i) { v[2 * i] = lo16<F16>(w[i]); v[2 * i + 1] = hi16<F16>(w[i]); }
     }
-    __device__ static void store(void* p, const float (&v)[E]) {
+    template <bool NT = false> __device__ static void store(void* p, const float (&v)[E]) {
         u32x4 w;
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = pack2<F16>(v[2 * i], v[2 * i + 1]);
-        *reinterpret_cast<u32x4*>(p) = w;
+        u32x4* a = reinterpret_cast<u32x4*>(p);
+        if (NT) __builtin_nontemporal_store(w, a); else *a = w;
     }
 };
 template <> struct Chunk<F32> {
     static constexpr int E = 4;
-    __device__ static void load(const void* p, float (&v)[E]) {
-        const f32x4 w = *reinterpret_cast<const f32x4*>(p);
+    template <bool NT = false> __device__ static void load(const void* p, float (&v)[E]) {
+        const f32x4* a = reinterpret_cast<const f32x4*>(p);
+        const f32x4 w = NT ? __builtin_nontemporal_load(a) : *a;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = w[i];
     }
-    __device__ static void store(void* p, const float (&v)[E]) {
-        *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+    template <bool NT = false> __device__ static void store(void* p, const float (&v)[E]) {
+        const f32x4 w = {v[0], v[1], v[2], v[3]};
+        f32x4* a = reinterpret_cast<f32x4*>(p);
+        if (NT) __builtin_nontemporal_store(w, a); else *a = w;
     }
 };
 
@@ -170,7 +179,7 @@ __global__ __launch_bounds__(threads_of<TPR>()) void softmax_online_kernel(Softm
         for (int i = 0; i < SCH; ++i) {
             const int ci = tid + i * TPR;
             if (ci < nchunk) {
-                C::load(xr + (int64_t)ci * EB, v[i]);
+                C::template load<true>(xr + (int64_t)ci * EB, v[i]);
 #pragma unroll
                 for (int e = 0; e < E; ++e) { v[i][e] *= p.c; m = fmaxf(m, v[i][e]); }
             } else {
@@ -198,7 +207,7 @@ __global__ __launch_bounds__(threads_of<TPR>()) void softmax_online_kernel(Softm
                 float o[E];
 #pragma unroll
                 for (int e = 0; e < E; ++e) o[e] = fast_exp2(v[i][e] - mu) * inv;
-                C::store(yr + (int64_t)ci * EB, o);
+                C::template store<true>(yr + (int64_t)ci * EB, o);
             }
         }
     } else {
@@ -221,10 +230,10 @@ __global__ __launch_bounds__(threads_of<TPR>()) void softmax_online_kernel(Softm
         const float mu = m == kNegInfS ? 0.f : m;
         for (int ci = tid; ci < nchunk; ci += TPR) {
             float v[E];
-            C::load(xr + (int64_t)ci * EB, v);
+            C::template load<true>(xr + (int64_t)ci * EB, v);  // the last read
 #pragma unroll
             for (int e = 0; e < E; ++e) v[e] = fast_exp2(v[e] * p.c - mu) * inv;
-            C::store(yr + (int64_t)ci * EB, v);
+            C::template store<true>(yr + (int64_t)ci * EB, v);
         }
     }
     if (live && tid == 0 && p.lse != nullptr) p.lse[row] = l > 0.f ? (m + log2f(l)) * kLn2 : kNegInfS;
@@ -255,7 +264,7 @@ __global__ __launch_bounds__(256) void softmax_online_short_kernel(SoftmaxParams
         for (int j = 0; j < SPR; ++j) {
             const int ci = lane + j * 64;
             if (live && ci < nch) {
-                C::load(xr + (int64_t)ci * EB, v[r][j]);
+                C::template load<true>(xr + (int64_t)ci * EB, v[r][j]);
             } else {
 #pragma unroll
                 for (int e = 0; e < E; ++e) v[r][j][e] = kNegInfS;
@@ -293,7 +302,7 @@ __global__ __launch_bounds__(256) void softmax_online_short_kernel(SoftmaxParams
                 float o[E];
 #pragma unroll
                 for (int e = 0; e < E; ++e) o[e] = fast_exp2(v[r][j][e] - mu) * inv;
-                C::store(yr + (int64_t)ci * EB, o);
+                C::template store<true>(yr + (int64_t)ci * EB, o);
             }
         }
         if (live && lane == 0 && p.lse != nullptr) p.lse[row0 + r] = l > 0.f ? (m[r] + log2f(l)) * kLn2 : kNegInfS;
