@@ -262,8 +262,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the fused kernel "
-              "is a single-GPU operation and multi-GPU runs are not part of this build.",
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library is a "
+              "single-GPU attention operator and has no multi-GPU path.",
               file=sys.stderr)
         return 2
 

@@ -17,7 +17,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped, not failed, where no GPU is visible; the HIP path
-    # itself still fails loudly when its library is missing on a GPU box.
+    # itself still fails loudly when its library is missing on a GPU machine.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
