@@ -29,8 +29,12 @@ SHAPES = {  # name: (B, H, Sq, Sk, causal, kv_len range, layout, extra workload 
     "large_scores": (1, 2, 400, 900, True, (500, 900), "bhsd", {"qk_mult": 4.0}),
     # scale * log2(e) > 1: queries are not pre-scaled
     "scale_above_one": (1, 2, 300, 700, False, None, "bhsd", {"scale": 2.0}),
-    # the largest scale that still pre-scales, on large scores
+    # scale * log2(e) ~ 1 on large scores
     "scale_at_one": (1, 2, 300, 700, False, None, "bhsd", {"scale": 0.69, "qk_mult": 2.0}),
+    # row maxima 15..30 above the reference (base 2): the running sum stays
+    # inside its range, but fp16 probabilities overflow 65504; the infinite
+    # row sum sends the tile to the exact-maximum path
+    "fp16_overflow_window": (1, 2, 300, 700, False, None, "bhsd", {"scale": 0.69}),
 }
 
 
