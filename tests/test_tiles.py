@@ -35,6 +35,8 @@ SHAPES = {  # name: (B, H, Sq, Sk, causal, kv_len range, layout, extra workload 
     # inside its range, but fp16 probabilities overflow 65504; the infinite
     # row sum sends the tile to the exact-maximum path
     "fp16_overflow_window": (1, 2, 300, 700, False, None, "bhsd", {"scale": 0.69}),
+    # scale 0 (uniform weights over the valid keys), with causal rows and padding
+    "scale_zero": (2, 2, 200, 333, True, (1, 333), "bshd", {"scale": 0.0}),
 }
 
 
