@@ -79,7 +79,7 @@ enum attn_dtype { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 };
 
 /*
  * Fused forward. Chooses between one fused kernel (prefill shapes) and the
- * split-over-keys pair of kernels (few query rows over many keys) as
+ * split-over-keys pair of kernels (one query row over many keys) as
  * attn_fwd_plan reports; the split path needs `workspace` of at least
  * attn_fwd_workspace_size bytes (NULL / 0 is fine when that size is 0).
  * scale must be finite and >= 0 (0 gives uniform weights over the valid keys).
@@ -93,8 +93,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * Returns 0 for arguments attn_fwd would reject. Host only. */
 size_t attn_fwd_workspace_size(int B, int H, int Sq, int Sk, int d, int dtype);
 
-/* The number of key splits attn_fwd will use (1 = single fused kernel; at
- * most 4 queries per head over at least 1024 keys always split).
+/* The number of key splits attn_fwd will use (1 = single fused kernel; a
+ * single query per head over at least 1024 keys always splits).
  * Host only; returns a status and writes *n_split on success. */
 int attn_fwd_plan(int B, int H, int Sq, int Sk, int d, int dtype, int* n_split);
 

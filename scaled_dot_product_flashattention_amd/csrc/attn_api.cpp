@@ -15,13 +15,15 @@
 namespace {
 
 constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
-// Split plan for few queries over many keys (measured on MI355X over
-// decode shapes of 8 to 1024 query rows and 4096 to 131072 keys): the
-// split kernels beat the fused kernel whenever each head has at most 4
-// queries (its 128-query tiles would be mostly empty), and they run best
-// with about 2 workgroups per compute unit and at most about 4096 keys per
-// split.
-constexpr int kSplitMaxQueries = 4;      // query rows per head at which the split path is used
+// Split plan for one query over many keys (measured on MI355X over decode
+// shapes of 8 to 1024 heads and 4096 to 131072 keys): the split kernels beat
+// the fused kernel for a single query per head (its 128-query tiles would be
+// almost empty), and run best with about 2 workgroups per compute unit and
+// at most about 4096 keys per split. They stream K and V once per query row,
+// so from two queries per head on, the fused kernel, which reads them once
+// per query tile, is faster (4 queries: 2441 us split against 764 us fused
+// at B8 H32 Sk32768).
+constexpr int kSplitMaxQueries = 1;      // query rows per head at which the split path is used
 constexpr int kSplitTargetGroups = 512;  // about 2 workgroups per compute unit
 constexpr int kSplitMaxKeys = 4096;      // keys per split, at most (more splits past that)
 constexpr int kSplitMinKeys = 512;       // keys per split, at least
