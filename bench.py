@@ -299,15 +299,15 @@ def main() -> int:
     kw = dict(scale=w.scale, causal=w.causal, layout=w.layout, kv_len=kv_len, out=o, lse=lse)
     tile = None
     if args.path == "fused":
-        nbytes = sdpa.attn_fwd_workspace_size(B, H, Sq, Sk, d, q.dtype)
+        nbytes = sdpa.attn_fwd_workspace_size(B, H, Sq, Sk, d, q.dtype, w.causal)
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
         step = lambda: sdpa.attn_fwd(q, k, v, workspace=ws, **kw)  # noqa: E731
-        n_split = sdpa.attn_fwd_plan(B, H, Sq, Sk, d, q.dtype)
-        if n_split == 1:
+        n_split = sdpa.attn_fwd_plan(B, H, Sq, Sk, d, q.dtype, w.causal)
+        if n_split == 1 or Sq > 1:  # the fused kernel, over all keys or over key ranges
             t_id = sdpa.attn_fwd_tile_choice(B, H, Sq, Sk, d, q.dtype, w.causal)
             tile = {"variant": t_id, **sdpa.attn_fwd_tile_info(d, q.dtype, t_id)}
     elif args.path == "splitk":
-        n_split = args.n_split or sdpa.attn_fwd_plan(B, H, Sq, Sk, d, q.dtype)
+        n_split = args.n_split or sdpa.attn_fwd_plan(B, H, Sq, Sk, d, q.dtype, w.causal)
         ws = torch.empty(sdpa.attn_splitk_workspace_size(B, H, Sq, d, n_split), dtype=torch.uint8,
                          device=dev)
         step = lambda: sdpa.attn_fwd_splitk(q, k, v, n_split=n_split, workspace=ws, **kw)  # noqa: E731
@@ -347,13 +347,19 @@ def main() -> int:
         del src, dst
 
     fl = flops(w)
-    decode = args.path == "splitk" or n_split > 1
+    # the split-over-keys kernels run for one query per head
+    splitk_kernels = args.path == "splitk" or (n_split > 1 and Sq == 1)
+    # below the ridge (peak FLOP/s over peak bytes/s) the K/V stream bounds
+    # the launch: few queries per head over many keys
+    peak_fl = PEAK_TFLOPS_F32 if w.dtype == "f32" else PEAK_TFLOPS_16
+    hbm_bound = splitk_kernels or fl / kv_bytes(w) < peak_fl * 1e3 / PEAK_HBM_GBS
     tflops = fl / (ms * 1e-3) / 1e12
-    if decode:
+    if hbm_bound:
         achieved = kv_bytes(w) / (ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
-        metric, value, unit = f"attention decode HBM GB/s, {w.description}", achieved, "GB/s"
+        what = "decode" if Sq == 1 else f"fwd ({args.path})"
+        metric, value, unit = f"attention {what} HBM GB/s, {w.description}", achieved, "GB/s"
     else:
         peak = PEAK_TFLOPS_F32 if w.dtype == "f32" else PEAK_TFLOPS_16
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
@@ -363,11 +369,11 @@ def main() -> int:
         else:
             metric = f"attention fwd TFLOP/s ({args.path}), {w.description}"
         value, unit = tflops, "TFLOP/s"
-    kind = "splitk" if decode else args.path
+    kind = "splitk" if splitk_kernels else args.path
     roof["traffic"] = None if relaid else stored_traffic(args.config, args.path, kind)
     roof["kernel_ms"] = round(ms, 5)
-    roof["algorithmic_units"] = ("bytes of K and V per launch" if decode else "FLOPs per launch")
-    roof["algorithmic_per_launch"] = kv_bytes(w) if decode else fl
+    roof["algorithmic_units"] = ("bytes of K and V per launch" if hbm_bound else "FLOPs per launch")
+    roof["algorithmic_per_launch"] = kv_bytes(w) if hbm_bound else fl
 
     line = {
         "metric": metric,

@@ -64,7 +64,8 @@ enum attn_status {
     ATTN_E_ALIGN = 4,       /* a pointer is not aligned as stated above          */
     ATTN_E_WORKSPACE = 5,   /* workspace / scratch NULL or smaller than required */
     ATTN_E_HIP = 6,         /* the HIP runtime reported an error at launch       */
-    ATTN_E_ARG = 7          /* scale negative, NaN or infinite; tile out of range */
+    ATTN_E_ARG = 7          /* scale negative, NaN or infinite; tile out of range;
+                             * n_split < 1 in attn_fwd_tiled                   */
 };
 
 enum attn_layout { ATTN_LAYOUT_BHSD = 0, ATTN_LAYOUT_BSHD = 1 };
@@ -78,9 +79,10 @@ enum attn_layout { ATTN_LAYOUT_BHSD = 0, ATTN_LAYOUT_BSHD = 1 };
 enum attn_dtype { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 };
 
 /*
- * Fused forward. Chooses between one fused kernel (prefill shapes) and the
- * split-over-keys pair of kernels (one query row over many keys) as
- * attn_fwd_plan reports; the split path needs `workspace` of at least
+ * Fused forward. Follows attn_fwd_plan: one fused kernel (prefill shapes),
+ * the fused kernel over key ranges plus a merge (few query tiles over long
+ * keys, 16-bit types), or the split-over-keys pair of kernels (one query row
+ * over many keys). A plan with key splits needs `workspace` of at least
  * attn_fwd_workspace_size bytes (NULL / 0 is fine when that size is 0).
  * scale must be finite and >= 0 (0 gives uniform weights over the valid keys).
  */
@@ -91,12 +93,18 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /* Bytes of workspace attn_fwd needs for this shape (0 when it plans no split).
  * Returns 0 for arguments attn_fwd would reject. Host only. */
-size_t attn_fwd_workspace_size(int B, int H, int Sq, int Sk, int d, int dtype);
+size_t attn_fwd_workspace_size(int B, int H, int Sq, int Sk, int d, int dtype, int causal);
 
-/* The number of key splits attn_fwd will use (1 = single fused kernel; a
- * single query per head over at least 1024 keys always splits).
+/* The number of key splits attn_fwd will use for these arguments. The keys
+ * a row can see count (with causal masking, at most Sq of them). 1: the
+ * fused kernel alone. More, with one query per head: the split-over-keys
+ * pair (a single query per head that sees at least 1024 keys always
+ * splits). More, with two or more queries per head (fp16/bf16 only): the
+ * fused kernel over key ranges, used when its (batch, head, 128-query tile)
+ * workgroups number fewer than 256 and a row sees at least 4096 keys, with
+ * about 256 workgroups in all and at least 1024 keys per range.
  * Host only; returns a status and writes *n_split on success. */
-int attn_fwd_plan(int B, int H, int Sq, int Sk, int d, int dtype, int* n_split);
+int attn_fwd_plan(int B, int H, int Sq, int Sk, int d, int dtype, int causal, int* n_split);
 
 /*
  * Tile variants of the fused kernel. The WebGPU page's section
@@ -106,7 +114,8 @@ int attn_fwd_plan(int B, int H, int Sq, int Sk, int d, int dtype, int* n_split);
  * timing every candidate on the GPU over a grid of query-row counts
  * (B*H*Sq) and key lengths, per head size and masking (the package's
  * autotune script writes it; the library must be rebuilt to use a new one).
- * attn_fwd and the prefill part of its plan use the table's choice.
+ * attn_fwd uses the table's choice for the fused kernel over all keys, and
+ * one fixed variant for the fused kernel over key ranges.
  */
 typedef struct attn_tile_info {
     int rows;      /* query rows per workgroup                              */
@@ -125,18 +134,31 @@ int attn_fwd_tile_count(int d, int dtype);
  * for a tile out of range. Host only. */
 int attn_fwd_tile_info(int d, int dtype, int tile, attn_tile_info* info);
 
-/* The variant the table picks for this shape, in *tile. Host only. */
+/* The variant attn_fwd's fused kernel runs for this shape, in *tile: the
+ * table's pick, or, where attn_fwd_plan gives the fused kernel key ranges,
+ * the variant for key ranges (attn_fwd_tiled with tile -1 makes the same
+ * choice for its n_split). Host only. */
 int attn_fwd_tile_choice(int B, int H, int Sq, int Sk, int d, int dtype, int causal, int* tile);
 
 /*
- * The fused single-kernel forward with tile variant `tile` (-1: the table's
- * choice), whatever the shape: never the split path, no workspace. Same
- * arguments and results as attn_fwd otherwise; a tile out of range is
- * ATTN_E_ARG. For tuning and testing every variant.
+ * The fused kernel with tile variant `tile` (-1: attn_fwd's choice) and
+ * n_split key ranges, whatever the shape; never the split-over-keys pair.
+ * n_split = 1: one kernel, no workspace (NULL / 0). n_split > 1 (fp16/bf16
+ * only, else ATTN_E_UNSUPPORTED): the keys are cut into n_split ranges of
+ * whole 64-key tiles (ceil(Sk / (64 n_split)) * 64 keys each; trailing
+ * ranges may be empty). Each (batch, head, query tile, range) workgroup
+ * writes, per query row, the unnormalised record of its range (running max,
+ * running sum, weighted sum of V) to `workspace`, which must hold
+ * attn_splitk_workspace_size(B, H, Sq, d, n_split) bytes, 16-byte aligned;
+ * the merge kernel of attn_fwd_splitk then combines the ranges by the block
+ * rule (the WebGPU page's FlashAttention section, §2.6 of the chapter).
+ * Same arguments and results as attn_fwd otherwise; a tile out of range or
+ * n_split < 1 is ATTN_E_ARG. For tuning and testing every variant.
  */
 int attn_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
-                   int dtype, const int32_t* kv_len, int tile, void* stream);
+                   int dtype, const int32_t* kv_len, int tile, int n_split, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /*
  * Split-over-keys forward with an explicit split count (the single-query

@@ -73,9 +73,9 @@ def load_library() -> ctypes.CDLL:
     L.attn_fwd_splitk.restype = i
     L.attn_fwd_naive.argtypes = tensors + [vp, sz, vp]
     L.attn_fwd_naive.restype = i
-    L.attn_fwd_workspace_size.argtypes = [i, i, i, i, i, i]
+    L.attn_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     L.attn_fwd_workspace_size.restype = sz
-    L.attn_fwd_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i)]
+    L.attn_fwd_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i)]
     L.attn_fwd_plan.restype = i
     L.attn_splitk_workspace_size.argtypes = [i, i, i, i, i]
     L.attn_splitk_workspace_size.restype = sz
@@ -91,7 +91,7 @@ def load_library() -> ctypes.CDLL:
     L.attn_fwd_tile_info.restype = i
     L.attn_fwd_tile_choice.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i)]
     L.attn_fwd_tile_choice.restype = i
-    L.attn_fwd_tiled.argtypes = tensors + [i, vp]
+    L.attn_fwd_tiled.argtypes = tensors + [i, i, vp, sz, vp]
     L.attn_fwd_tiled.restype = i
     L.attn_status_string.argtypes = [i]
     L.attn_status_string.restype = ctypes.c_char_p
@@ -116,9 +116,11 @@ def dtype_code(dtype: torch.dtype) -> int:
     return _DTYPE[dtype]
 
 
-def attn_fwd_plan(B: int, H: int, Sq: int, Sk: int, d: int, dtype: torch.dtype) -> int:
+def attn_fwd_plan(B: int, H: int, Sq: int, Sk: int, d: int, dtype: torch.dtype,
+                  causal: bool = False) -> int:
     n = ctypes.c_int(0)
-    rc = load_library().attn_fwd_plan(B, H, Sq, Sk, d, dtype_code(dtype), ctypes.byref(n))
+    rc = load_library().attn_fwd_plan(B, H, Sq, Sk, d, dtype_code(dtype), int(bool(causal)),
+                                      ctypes.byref(n))
     if rc:
         raise AttnError("attn_fwd_plan", rc)
     return n.value
@@ -146,8 +148,10 @@ def attn_fwd_tile_choice(B: int, H: int, Sq: int, Sk: int, d: int, dtype: torch.
     return t.value
 
 
-def attn_fwd_workspace_size(B: int, H: int, Sq: int, Sk: int, d: int, dtype: torch.dtype) -> int:
-    return load_library().attn_fwd_workspace_size(B, H, Sq, Sk, d, dtype_code(dtype))
+def attn_fwd_workspace_size(B: int, H: int, Sq: int, Sk: int, d: int, dtype: torch.dtype,
+                            causal: bool = False) -> int:
+    return load_library().attn_fwd_workspace_size(B, H, Sq, Sk, d, dtype_code(dtype),
+                                                  int(bool(causal)))
 
 
 def attn_splitk_workspace_size(B: int, H: int, Sq: int, d: int, n_split: int) -> int:
@@ -245,7 +249,7 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, layout="bhsd", kv_len=None, r
     (B, H, Sq, Sk, d), kv_len, scale, o, lse = _prepare(q, k, v, layout, kv_len, scale, lse,
                                                         return_lse, out)
     dt = dtype_code(q.dtype)
-    nbytes = attn_fwd_workspace_size(B, H, Sq, Sk, d, q.dtype)
+    nbytes = attn_fwd_workspace_size(B, H, Sq, Sk, d, q.dtype, causal)
     ws = _scratch(nbytes, q.device, workspace)
     rc = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq, Sk, d,
                                  scale, int(bool(causal)), layout_code(layout), dt, _ptr(kv_len),
@@ -256,15 +260,21 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, layout="bhsd", kv_len=None, r
     return o, lse
 
 
-def attn_fwd_tiled(q, k, v, *, tile=-1, scale=None, causal=False, layout="bhsd", kv_len=None,
-                   return_lse=True, out=None, lse=None, stream=None):
+def attn_fwd_tiled(q, k, v, *, tile=-1, n_split=1, scale=None, causal=False, layout="bhsd",
+                   kv_len=None, return_lse=True, out=None, lse=None, workspace=None, stream=None):
     """The fused kernel with tile variant ``tile`` (-1: the tuned table's
-    choice), never the split path. Returns (o, lse)."""
+    choice) over ``n_split`` key ranges (more than 1: per-range records in
+    the workspace, then the merge), never the split-over-keys pair.
+    Returns (o, lse)."""
     (B, H, Sq, Sk, d), kv_len, scale, o, lse = _prepare(q, k, v, layout, kv_len, scale, lse,
                                                         return_lse, out)
+    n_split = int(n_split)
+    nbytes = attn_splitk_workspace_size(B, H, Sq, d, n_split) if n_split > 1 else 0
+    ws = _scratch(nbytes, q.device, workspace)
     rc = load_library().attn_fwd_tiled(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq, Sk,
                                        d, scale, int(bool(causal)), layout_code(layout),
-                                       dtype_code(q.dtype), _ptr(kv_len), int(tile),
+                                       dtype_code(q.dtype), _ptr(kv_len), int(tile), n_split,
+                                       _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                        _stream(q, stream))
     if rc:
         raise AttnError("attn_fwd_tiled", rc)

@@ -27,6 +27,14 @@ constexpr int kSplitMaxQueries = 1;      // query rows per head at which the spl
 constexpr int kSplitTargetGroups = 512;  // about 2 workgroups per compute unit
 constexpr int kSplitMaxKeys = 4096;      // keys per split, at most (more splits past that)
 constexpr int kSplitMinKeys = 512;       // keys per split, at least
+// Key splits of the fused 16-bit kernel, for two or more queries per head:
+// when its (batch, head, 128-query tile) workgroups would not fill the
+// compute units and the keys are long, each workgroup takes one key range
+// and the merge kernel combines the ranges' records.
+constexpr int kFusedSplitTargetGroups = 256;  // split below this many workgroups, up to about this many
+constexpr int kFusedSplitMinKeys = 1024;      // keys per range, at least
+constexpr int kFusedSplitMinTotal = 4096;     // keys per row, at least, to split at all
+constexpr int kFusedSplitMax = 64;            // ranges, at most
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -62,8 +70,22 @@ int check_call(const void* q, const void* k, const void* v, const void* o, const
     return ATTN_OK;
 }
 
-int plan_splits(int B, int H, int Sq, int Sk) {
-    if (Sq > kSplitMaxQueries) return 1;
+// Key splits for the fused kernel (16-bit types, Sq > kSplitMaxQueries);
+// Sk is the keys a row can see
+int plan_fused_splits(int B, int H, int Sq, int Sk, int dtype) {
+    if (dtype == ATTN_F32 || Sk < kFusedSplitMinTotal) return 1;
+    const int64_t groups = (int64_t)B * H * ((Sq + 127) / 128);
+    if (groups >= kFusedSplitTargetGroups) return 1;
+    int64_t n = (kFusedSplitTargetGroups + groups - 1) / groups;
+    if (n > Sk / kFusedSplitMinKeys) n = Sk / kFusedSplitMinKeys;
+    if (n > kFusedSplitMax) n = kFusedSplitMax;
+    return n >= 2 ? (int)n : 1;
+}
+
+int plan_splits(int B, int H, int Sq, int Sk, int dtype, int causal) {
+    // a causal row i sees keys 0 .. i: no row sees more than Sq keys
+    if (causal && Sq < Sk) Sk = Sq;
+    if (Sq > kSplitMaxQueries) return plan_fused_splits(B, H, Sq, Sk, dtype);
     const int64_t rows = (int64_t)B * H * Sq;
     int64_t n = (kSplitTargetGroups + rows - 1) / rows;
     if (n < Sk / kSplitMaxKeys) n = Sk / kSplitMaxKeys;
@@ -103,11 +125,11 @@ int status_of(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
 
 extern "C" {
 
-int attn_fwd_plan(int B, int H, int Sq, int Sk, int d, int dtype, int* n_split) {
+int attn_fwd_plan(int B, int H, int Sq, int Sk, int d, int dtype, int causal, int* n_split) {
     if (!n_split) return ATTN_E_NULLPTR;
     int rc = check_shape(B, H, Sq, Sk, d, ATTN_LAYOUT_BHSD, dtype);
     if (rc != ATTN_OK) return rc;
-    *n_split = plan_splits(B, H, Sq, Sk);
+    *n_split = plan_splits(B, H, Sq, Sk, dtype, causal);
     return ATTN_OK;
 }
 
@@ -116,9 +138,9 @@ size_t attn_splitk_workspace_size(int B, int H, int Sq, int d, int n_split) {
     return attn::splitk_workspace_bytes(B, H, Sq, d, n_split);
 }
 
-size_t attn_fwd_workspace_size(int B, int H, int Sq, int Sk, int d, int dtype) {
+size_t attn_fwd_workspace_size(int B, int H, int Sq, int Sk, int d, int dtype, int causal) {
     if (check_shape(B, H, Sq, Sk, d, ATTN_LAYOUT_BHSD, dtype) != ATTN_OK) return 0;
-    const int n = plan_splits(B, H, Sq, Sk);
+    const int n = plan_splits(B, H, Sq, Sk, dtype, causal);
     return n > 1 ? attn::splitk_workspace_bytes(B, H, Sq, d, n) : 0;
 }
 
@@ -142,12 +164,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              void* stream) {
     int rc = check_call(q, k, v, o, lse, B, H, Sq, Sk, d, scale, layout, dtype, kv_len);
     if (rc != ATTN_OK) return rc;
-    const int n = plan_splits(B, H, Sq, Sk);
-    if (n > 1)
+    const int n = plan_splits(B, H, Sq, Sk, dtype, causal);
+    if (n > 1 && Sq <= kSplitMaxQueries)
         return attn_fwd_splitk(q, k, v, o, lse, B, H, Sq, Sk, d, scale, causal, layout, dtype, kv_len, n,
                                workspace, workspace_bytes, stream);
-    const attn::FwdArgs a = make_args(q, k, v, o, lse, B, H, Sq, Sk, d, scale, causal, layout, dtype, kv_len);
-    return status_of(attn::run_prefill(a, static_cast<hipStream_t>(stream)));
+    return attn_fwd_tiled(q, k, v, o, lse, B, H, Sq, Sk, d, scale, causal, layout, dtype, kv_len, -1, n,
+                          workspace, workspace_bytes, stream);
 }
 
 int attn_fwd_tile_count(int d, int dtype) {
@@ -173,18 +195,32 @@ int attn_fwd_tile_choice(int B, int H, int Sq, int Sk, int d, int dtype, int cau
     if (!tile) return ATTN_E_NULLPTR;
     int rc = check_shape(B, H, Sq, Sk, d, ATTN_LAYOUT_BHSD, dtype);
     if (rc != ATTN_OK) return rc;
-    *tile = attn::prefill_tile_choice(B, H, Sq, Sk, d, dtype, causal != 0);
+    const int n = plan_splits(B, H, Sq, Sk, dtype, causal);
+    *tile = attn::prefill_tile_choice(B, H, Sq, Sk, d, dtype, causal != 0,
+                                      Sq > kSplitMaxQueries ? n : 1);
     return ATTN_OK;
 }
 
 int attn_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
-                   int dtype, const int32_t* kv_len, int tile, void* stream) {
+                   int dtype, const int32_t* kv_len, int tile, int n_split, void* workspace,
+                   size_t workspace_bytes, void* stream) {
     int rc = check_call(q, k, v, o, lse, B, H, Sq, Sk, d, scale, layout, dtype, kv_len);
     if (rc != ATTN_OK) return rc;
-    if (tile < -1 || tile >= attn::prefill_tile_count(d, dtype)) return ATTN_E_ARG;
+    if (tile < -1 || tile >= attn::prefill_tile_count(d, dtype) || n_split < 1) return ATTN_E_ARG;
+    if (n_split > 1) {
+        if (dtype == ATTN_F32) return ATTN_E_UNSUPPORTED;
+        // record indices and key-range ends (ranges are whole 64-key tiles) fit in int32
+        if ((int64_t)B * H * Sq * n_split > INT_MAX || (int64_t)Sk + (int64_t)n_split * 64 > INT_MAX)
+            return ATTN_E_SHAPE;
+        const size_t need = attn::splitk_workspace_bytes(B, H, Sq, d, n_split);
+        if (!workspace || workspace_bytes < need) return ATTN_E_WORKSPACE;
+        if (!aligned(workspace, 16)) return ATTN_E_ALIGN;
+    }
     attn::FwdArgs a = make_args(q, k, v, o, lse, B, H, Sq, Sk, d, scale, causal, layout, dtype, kv_len);
     a.tile = tile;
+    a.n_split = n_split;
+    a.ws = n_split > 1 ? workspace : nullptr;
     return status_of(attn::run_prefill(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -472,7 +472,7 @@ hipError_t launch_prefill(const FwdArgs& a, hipStream_t stream) {
 
 hipError_t run_prefill(const FwdArgs& a, hipStream_t stream) {
     if (a.dtype != 0) return run_prefill16(a, stream);
-    if (a.tile > 0) return hipErrorInvalidValue;  // fp32 has one variant
+    if (a.tile > 0 || a.n_split > 1) return hipErrorInvalidValue;  // fp32: one variant, no key splits
     return a.d == 64 ? launch_prefill<F32, 64, 1, false>(a, stream) : launch_prefill<F32, 128, 1, false>(a, stream);
 }
 
@@ -490,8 +490,8 @@ bool prefill_tile_info(int d, int dtype, int tile, TileInfo* out) {
     return true;
 }
 
-int prefill_tile_choice(int B, int H, int Sq, int Sk, int d, int dtype, int causal) {
-    return dtype == 0 ? 0 : prefill16_tile_choice(B, H, Sq, Sk, d, causal);
+int prefill_tile_choice(int B, int H, int Sq, int Sk, int d, int dtype, int causal, int n_split) {
+    return dtype == 0 ? 0 : prefill16_tile_choice(B, H, Sq, Sk, d, causal, n_split);
 }
 
 }  // namespace attn

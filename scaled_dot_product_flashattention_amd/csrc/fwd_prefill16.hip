@@ -73,6 +73,11 @@ struct Prefill16Params {
     int causal;
     int n_qtiles;
     int remap;  // grid size is a multiple of 8: keep each head's tiles on one XCD
+    // key splits (SPLIT kernels): workgroup split s takes keys
+    // [s * chunk, (s + 1) * chunk) and writes its (m, l, o) records to ws
+    float* ws;
+    int n_split;
+    int chunk;
 };
 
 // LDS of one workgroup: the K/V ring, reused for the output staging rows
@@ -130,7 +135,12 @@ __device__ __forceinline__ bool sum_out_of_range(float l) {
 //   NST    LDS ring stages (NST - 2 tiles in flight ahead)
 //   KSPLIT 1: 4 waves, each over all keys of a tile; 2: 8 waves, wave w
 //          takes key half w / 4 of every tile for the queries of wave w % 4
-template <typename Tag, int D, int NQ, int BN, int NST, int KSPLIT>
+//   SPLIT  each workgroup takes one range of p.chunk keys and, instead of
+//          O and LSE, writes per query row the record (m, l, -, -, o[D]) of
+//          its range: the reference max m (log2 units; -inf when l = 0), the
+//          sum l against it and the unnormalised output o. The records of
+//          the ranges of a row combine exactly by the block rule.
+template <typename Tag, int D, int NQ, int BN, int NST, int KSPLIT, bool SPLIT>
 __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel(Prefill16Params p) {
     constexpr int NT = 256 * KSPLIT;               // threads
     constexpr int KBW = BN / 32 / KSPLIT;          // 32-key blocks per wave and tile
@@ -171,7 +181,15 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
     constexpr int BM = 4 * 32 * NQ;
     const int G = gridDim.x;
     const int g = blockIdx.x;
-    const int w = p.remap ? (g & 7) * (G >> 3) + (g >> 3) : g;
+    int w = p.remap ? (g & 7) * (G >> 3) + (g >> 3) : g;
+    // query tiles innermost: the tiles of one key range of a head run
+    // together and share its K/V in L2
+    int split = 0;
+    if constexpr (SPLIT) {
+        const int rest = w / p.n_qtiles;
+        split = rest % p.n_split;
+        w = (rest / p.n_split) * p.n_qtiles + (w - rest * p.n_qtiles);
+    }
     const int bh = w / p.n_qtiles;
     int qt = w - bh * p.n_qtiles;
     if (p.causal) qt = p.n_qtiles - 1 - qt;  // longest causal tiles first
@@ -182,7 +200,10 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
     const int q0 = qt * BM;
     const int q_end = min(q0 + BM, p.Sq);
     const int kend = p.causal ? min(nb, q_end) : nb;  // keys any row of the tile can see
-    const int ntiles = (kend + BN - 1) / BN;
+    const int key_lo = SPLIT ? split * p.chunk : 0;   // this workgroup's keys: [key_lo, key_hi)
+    const int key_hi = SPLIT ? min(key_lo + p.chunk, kend) : kend;
+    const int ntiles = key_hi > key_lo ? (key_hi - key_lo + BN - 1) / BN : 0;
+    const int lim_hi = SPLIT ? key_hi : nb;  // keys from here on are masked for every row
 
     const T* qp = static_cast<const T*>(p.q) + p.sq.head(b, h);
     const T* kp = static_cast<const T*>(p.k) + p.sk.head(b, h);
@@ -191,9 +212,9 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
 
     const int qw0 = q0 + wq * 32 * NQ;  // first query row of this wave
     // Waves past the last query row compute on zero queries and store nothing.
-    const int wave_lim_min = p.causal ? min(nb, qw0 + 1) : nb;  // keys past this need masks
+    const int wave_lim_min = p.causal ? min(lim_hi, qw0 + 1) : lim_hi;  // keys past this need masks
     // first key of this wave's part of `tile`
-    auto wkey0 = [&](int tile) __attribute__((always_inline)) { return tile * BN + kb0 * 32; };
+    auto wkey0 = [&](int tile) __attribute__((always_inline)) { return key_lo + tile * BN + kb0 * 32; };
 
     // Q operands (B of S^T = K Q^T), in registers for the whole loop: K-step
     // s holds q[row][16s + 8h .. +7]. Loaded with the first DMA tile below.
@@ -215,7 +236,7 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)smem;
     auto issue_tile = [&](int tile) __attribute__((always_inline)) {
         const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + (tile % NST) * STAGE_B + wave * 1024);
-        const int key0 = tile * BN;
+        const int key0 = key_lo + tile * BN;
         if (key0 + BN <= nb) {
             const T* kt = kp + key0 * p.sk.s;
             const T* vt = vp + key0 * p.sk.s;
@@ -343,7 +364,7 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
 #pragma unroll
         for (int gq = 0; gq < NQ; ++gq) {
             const int qi = qw0 + gq * 32 + n32;
-            const int lim = p.causal ? min(nb, qi + 1) : nb;
+            const int lim = p.causal ? min(lim_hi, qi + 1) : lim_hi;
 #pragma unroll
             for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
@@ -540,6 +561,34 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
         __syncthreads();
     }
 
+    // ---- epilogue of a key range: the rows' records --------------------------
+    // Lane (n32, h) holds o[d] for d = db*32 + 8jj + 4h + e, e = 0..3: one
+    // 16-byte store each.
+    if constexpr (SPLIT) {
+        if (kh == 0) {
+#pragma unroll
+            for (int gq = 0; gq < NQ; ++gq) {
+                const int qi = qw0 + gq * 32 + n32;
+                if (qi >= p.Sq) continue;
+                const float lt = l_run[gq] + swap_halves(l_run[gq]);
+                float* rec = p.ws + ((((int64_t)b * p.H + h) * p.Sq + qi) * p.n_split + split) * (D + 4);
+                if (hh == 0) {
+                    rec[0] = lt > 0.f ? m_run[gq] : kNegInf;
+                    rec[1] = lt;
+                }
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const f32x16& ov = oacc[gq][db];
+                        *reinterpret_cast<f32x4*>(rec + 4 + db * 32 + 8 * jj + 4 * hh) =
+                            f32x4{ov[4 * jj], ov[4 * jj + 1], ov[4 * jj + 2], ov[4 * jj + 3]};
+                    }
+            }
+        }
+        return;
+    }
+
     // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2 -------------------
     if (kh == 0) {
         T* Os = reinterpret_cast<T*>(smem) + wq * 32 * NQ * OROW;
@@ -576,7 +625,7 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
     }
 }
 
-template <typename Tag, int D, int NQ, int BN, int NST, int KSPLIT>
+template <typename Tag, int D, int NQ, int BN, int NST, int KSPLIT, bool SPLIT>
 hipError_t launch16(const FwdArgs& a, hipStream_t stream) {
     constexpr int BM = 4 * 32 * NQ;
     Prefill16Params p;
@@ -597,12 +646,18 @@ hipError_t launch16(const FwdArgs& a, hipStream_t stream) {
     p.c = a.scale > 0.f ? a.scale * kLog2e : 1e-30f;
     p.causal = a.causal ? 1 : 0;
     p.n_qtiles = (a.Sq + BM - 1) / BM;
-    const int64_t grid = (int64_t)p.n_qtiles * a.B * a.H;
+    p.ws = static_cast<float*>(a.ws);
+    p.n_split = SPLIT ? a.n_split : 1;
+    // whole tiles per key range
+    p.chunk = SPLIT ? (a.Sk + a.n_split * BN - 1) / (a.n_split * BN) * BN : a.Sk;
+    const int64_t grid = (int64_t)p.n_qtiles * a.B * a.H * p.n_split;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     p.remap = (grid % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((fwd_prefill16_kernel<Tag, D, NQ, BN, NST, KSPLIT>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((fwd_prefill16_kernel<Tag, D, NQ, BN, NST, KSPLIT, SPLIT>), dim3((unsigned)grid),
                        dim3(256 * KSPLIT), 0, stream, p);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !SPLIT) return e;
+    return run_splitk_merge(a, a.n_split, a.ws, stream);
 }
 
 // ---- tile variants and their choice ----------------------------------------
@@ -612,11 +667,12 @@ hipError_t launch16(const FwdArgs& a, hipStream_t stream) {
 // names the variant per head size, masking, key length and query rows.
 struct Variant16 {
     int nq, bn, nst, ksplit, lds;
-    hipError_t (*run[2])(const FwdArgs&, hipStream_t);  // fp16, bf16
+    hipError_t (*run[2][2])(const FwdArgs&, hipStream_t);  // [whole keys, key splits][fp16, bf16]
 };
-#define ATTN_VARIANT16(D, NQ, BN, NST, KS)                                       \
-    {NQ, BN, NST, KS, lds_bytes16(D, NQ, BN, NST, KS),                           \
-     {&launch16<F16, D, NQ, BN, NST, KS>, &launch16<BF16, D, NQ, BN, NST, KS>}}
+#define ATTN_VARIANT16(D, NQ, BN, NST, KS)                                                   \
+    {NQ, BN, NST, KS, lds_bytes16(D, NQ, BN, NST, KS),                                       \
+     {{&launch16<F16, D, NQ, BN, NST, KS, false>, &launch16<BF16, D, NQ, BN, NST, KS, false>}, \
+      {&launch16<F16, D, NQ, BN, NST, KS, true>, &launch16<BF16, D, NQ, BN, NST, KS, true>}}}
 const Variant16 kVariants64[] = {
     ATTN_VARIANT16(64, 1, 64, 5, 1),  // 0: 128 queries x 64 keys, 4 waves
     ATTN_VARIANT16(64, 1, 64, 4, 1),  // 1: same, shorter ring
@@ -634,6 +690,15 @@ constexpr int kNumVariants64 = sizeof(kVariants64) / sizeof(kVariants64[0]);
 constexpr int kNumVariants128 = sizeof(kVariants128) / sizeof(kVariants128[0]);
 
 #include "tile_table.inc"
+
+// With key ranges the grid holds about one workgroup per compute unit, and
+// each workgroup waits on its loads more than on its arithmetic: the variant
+// with eight waves (two key halves of 64-key tiles, 128 queries) was the
+// fastest, or within a few percent of it, on every few-head shape measured
+// on gfx950 (32 to 128 query tiles over 4096 to 65536 keys, both head sizes).
+constexpr int kRangeTile64 = 3;
+constexpr int kRangeTile128 = 3;
+static_assert(kRangeTile64 < kNumVariants64 && kRangeTile128 < kNumVariants128, "key-range variant");
 
 // Bucket of x on a log2 grid starting at 2^lo with n points (nearest point).
 int log2_bucket(int64_t x, int lo, int n) {
@@ -660,17 +725,19 @@ bool prefill16_tile_info(int d, int tile, TileInfo* out) {
     return true;
 }
 
-int prefill16_tile_choice(int B, int H, int Sq, int Sk, int d, int causal) {
+int prefill16_tile_choice(int B, int H, int Sq, int Sk, int d, int causal, int n_split) {
+    if (n_split > 1) return d == 128 ? kRangeTile128 : kRangeTile64;
     const int r = log2_bucket((int64_t)B * H * Sq, kTuneRowsLog2Min, kTuneRowsBuckets);
     const int k = log2_bucket(Sk, kTuneKeysLog2Min, kTuneKeysBuckets);
     return kTileTable[d == 128 ? 1 : 0][causal ? 1 : 0][r][k];
 }
 
 hipError_t run_prefill16(const FwdArgs& a, hipStream_t stream) {
-    const int tile = a.tile >= 0 ? a.tile : prefill16_tile_choice(a.B, a.H, a.Sq, a.Sk, a.d, a.causal);
+    const int tile = a.tile >= 0 ? a.tile : prefill16_tile_choice(a.B, a.H, a.Sq, a.Sk, a.d, a.causal, a.n_split);
     if (tile < 0 || tile >= prefill16_tile_count(a.d)) return hipErrorInvalidValue;
     const Variant16& v = a.d == 128 ? kVariants128[tile] : kVariants64[tile];
-    return v.run[a.dtype == 2 ? 1 : 0](a, stream);
+    if (a.n_split > 1 && a.ws == nullptr) return hipErrorInvalidValue;
+    return v.run[a.n_split > 1 ? 1 : 0][a.dtype == 2 ? 1 : 0](a, stream);
 }
 
 }  // namespace attn

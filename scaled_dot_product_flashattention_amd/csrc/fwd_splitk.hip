@@ -212,32 +212,81 @@ __global__ __launch_bounds__(256) void splitk_partial_kernel(SplitParams p) {
     }
 }
 
-template <typename Tag, int D>
-__global__ __launch_bounds__(128) void splitk_merge_kernel(SplitParams p) {
+// Kernel 2. WPR waves per row (1 for many rows over few splits, 4 for few
+// rows over many splits), 4 waves per workgroup. Every wave of a row first
+// takes the row's max M over all splits' m (lane s reads m_s); wave j of the
+// row then sums the splits s = j, j + WPR, ... with weights 2^(m_s - M), its
+// lane holding elements EPL*lane .. EPL*lane + EPL-1 of o. With WPR > 1 the
+// waves' sums meet in LDS. A split with nothing accumulated has m = -inf and
+// weight 0; a row with no valid key gets O = 0 and LSE = -inf.
+template <typename Tag, int D, int WPR>
+__global__ __launch_bounds__(256) void splitk_merge_kernel(SplitParams p) {
     using T = typename Tag::storage;
-    const int row = blockIdx.x;  // (b*H + h)*Sq + i
-    const int i = row % p.Sq;
-    const int h = (row / p.Sq) % p.H;
-    const int b = row / (p.Sq * p.H);
-    const int t = threadIdx.x;
-    const float* part = p.ws + (int64_t)row * p.n_split * ws_stride(D);
+    constexpr int EPL = D / 64;
+    constexpr int RPB = 4 / WPR;  // rows per workgroup
+    static_assert(D % 64 == 0 && 4 % WPR == 0, "merge shape");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sub = wave % WPR;
+    const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+    const int64_t row = (int64_t)blockIdx.x * RPB + wave / WPR;
+    const bool live = row < rows;
+    const float* part = p.ws + (live ? row : 0) * p.n_split * ws_stride(D);
 
     float M = kNegInf;
-    for (int s = 0; s < p.n_split; ++s) M = fmaxf(M, part[s * ws_stride(D)]);
+    for (int s = lane; s < p.n_split; s += 64) M = fmaxf(M, part[(int64_t)s * ws_stride(D)]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     const float M_use = (M == kNegInf) ? 0.f : M;
-    float L = 0.f, A = 0.f;
-    for (int s = 0; s < p.n_split; ++s) {
-        const float* ps = part + s * ws_stride(D);
+    float L = 0.f;
+    float A[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) A[e] = 0.f;
+#pragma unroll 4
+    for (int s = sub; s < p.n_split; s += WPR) {
+        const float* ps = part + (int64_t)s * ws_stride(D);
         const float wgt = fast_exp2(ps[0] - M_use);
         L = fmaf(wgt, ps[1], L);
-        if (t < D) A = fmaf(wgt, ps[4 + t], A);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) A[e] = fmaf(wgt, ps[4 + EPL * lane + e], A[e]);
     }
-    if (t < D) {
-        const float out = L > 0.f ? A / L : 0.f;
-        T* orow = static_cast<T*>(p.o) + p.sq.head(b, h) + (int64_t)i * p.sq.s;
-        orow[t] = to_storage<Tag>(out);
+    if constexpr (WPR > 1) {
+        __shared__ float red[4][EPL * 64 + 1];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) red[wave][EPL * lane + e] = A[e];
+        if (lane == 0) red[wave][EPL * 64] = L;
+        __syncthreads();
+        if (sub == 0) {
+            for (int j = 1; j < WPR; ++j) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) A[e] += red[wave + j][EPL * lane + e];
+                L += red[wave + j][EPL * 64];
+            }
+        }
     }
-    if (t == 0 && p.lse != nullptr) p.lse[row] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
+    if (!live || sub != 0) return;
+    const int i = (int)(row % p.Sq);
+    const int h = (int)((row / p.Sq) % p.H);
+    const int b = (int)(row / ((int64_t)p.Sq * p.H));
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    T* orow = static_cast<T*>(p.o) + p.sq.head(b, h) + (int64_t)i * p.sq.s;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) orow[EPL * lane + e] = to_storage<Tag>(A[e] * inv);
+    if (lane == 0 && p.lse != nullptr) p.lse[row] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
+}
+
+// The merge for (rows, n_split): four waves per row when few rows share many
+// splits, one otherwise.
+template <typename Tag, int D>
+hipError_t launch_merge_kernel(const SplitParams& p, hipStream_t stream) {
+    const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+    if (rows > 0x7fffffff) return hipErrorInvalidValue;
+    if (p.n_split >= 16 && rows < 4096)
+        hipLaunchKernelGGL((splitk_merge_kernel<Tag, D, 4>), dim3((unsigned)rows), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((splitk_merge_kernel<Tag, D, 1>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                           stream, p);
+    return hipGetLastError();
 }
 
 template <typename Tag, int D>
@@ -266,11 +315,35 @@ hipError_t launch_splitk(const FwdArgs& a, int n_split, void* workspace, hipStre
     hipLaunchKernelGGL((splitk_partial_kernel<Tag, D>), dim3((unsigned)grid), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((splitk_merge_kernel<Tag, D>), dim3((unsigned)rows), dim3(128), 0, stream, p);
-    return hipGetLastError();
+    return launch_merge_kernel<Tag, D>(p, stream);
+}
+
+template <typename Tag, int D>
+hipError_t launch_merge(const FwdArgs& a, int n_split, const void* workspace, hipStream_t stream) {
+    SplitParams p = {};
+    p.o = a.o;
+    p.lse = a.lse;
+    p.ws = static_cast<float*>(const_cast<void*>(workspace));
+    p.sq = make_strides(a.layout, a.H, a.Sq, a.d);
+    p.B = a.B;
+    p.H = a.H;
+    p.Sq = a.Sq;
+    p.n_split = n_split;
+    return launch_merge_kernel<Tag, D>(p, stream);
 }
 
 }  // namespace
+
+hipError_t run_splitk_merge(const FwdArgs& a, int n_split, const void* workspace, hipStream_t stream) {
+    switch (a.dtype) {
+    case 2: return a.d == 64 ? launch_merge<BF16, 64>(a, n_split, workspace, stream)
+                             : launch_merge<BF16, 128>(a, n_split, workspace, stream);
+    case 1: return a.d == 64 ? launch_merge<F16, 64>(a, n_split, workspace, stream)
+                             : launch_merge<F16, 128>(a, n_split, workspace, stream);
+    default: return a.d == 64 ? launch_merge<F32, 64>(a, n_split, workspace, stream)
+                              : launch_merge<F32, 128>(a, n_split, workspace, stream);
+    }
+}
 
 size_t splitk_workspace_bytes(int B, int H, int Sq, int d, int n_split) {
     return (size_t)B * H * Sq * (size_t)n_split * ws_stride(d) * sizeof(float);

@@ -21,6 +21,10 @@ struct FwdArgs {
     int layout;     // 0 = [B,H,S,d], 1 = [B,S,H,d], 0x10000 | g = groups of g heads
     int dtype;      // 0 = fp32, 1 = fp16, 2 = bf16
     int tile = -1;  // fused kernel's tile variant; -1 = the tuned table's choice
+    // fused kernel over key splits: n_split > 1 writes per-split (m, l, o)
+    // records to `ws` (the split-K layout) and merges them
+    int n_split = 1;
+    void* ws = nullptr;
 };
 
 // Fused single-kernel forward (any shape); 16-bit inputs go to run_prefill16.
@@ -33,14 +37,17 @@ struct TileInfo {
 };
 int prefill_tile_count(int d, int dtype);
 bool prefill_tile_info(int d, int dtype, int tile, TileInfo* out);
-int prefill_tile_choice(int B, int H, int Sq, int Sk, int d, int dtype, int causal);
+// the variant the fused kernel runs for this shape over n_split key ranges
+int prefill_tile_choice(int B, int H, int Sq, int Sk, int d, int dtype, int causal, int n_split);
 int prefill16_tile_count(int d);
 bool prefill16_tile_info(int d, int tile, TileInfo* out);
-int prefill16_tile_choice(int B, int H, int Sq, int Sk, int d, int causal);
+int prefill16_tile_choice(int B, int H, int Sq, int Sk, int d, int causal, int n_split);
 
 // Split-over-keys forward: partial kernel + merge kernel.
 size_t splitk_workspace_bytes(int B, int H, int Sq, int d, int n_split);
 hipError_t run_splitk(const FwdArgs& a, int n_split, void* workspace, hipStream_t stream);
+// The merge kernel alone, over records another kernel wrote.
+hipError_t run_splitk_merge(const FwdArgs& a, int n_split, const void* workspace, hipStream_t stream);
 
 // QKV projection: x [B,S,D] times the out-major weight [3*H*d, D] into q, k, v.
 struct QkvArgs {

@@ -41,8 +41,11 @@ def run_path(path, q, k, v, w: Workload, kv_len, n_split=None, scale=None):
         return sdpa.attn_fwd_splitk(q, k, v, n_split=n_split, **kw)
     if path == "naive":
         return sdpa.attn_fwd_naive(q, k, v, **kw)
-    if path.startswith("tile:"):  # the fused kernel with a forced tile variant
-        return sdpa.attn_fwd_tiled(q, k, v, tile=int(path[5:]), **kw)
+    if path.startswith("tile:"):  # the fused kernel with a forced tile variant ("tile:T")
+        # and key splits ("tile:T:N")
+        parts = path.split(":")
+        return sdpa.attn_fwd_tiled(q, k, v, tile=int(parts[1]),
+                                   n_split=int(parts[2]) if len(parts) > 2 else 1, **kw)
     raise ValueError(path)
 
 

@@ -98,9 +98,9 @@ def test_workspace_statuses(lib):
     # decode shape: the plan splits, so attn_fwd needs a workspace
     shape = dict(B=8, H=32, Sq=1, Sk=32768, d=128)
     n = ctypes.c_int(0)
-    assert lib.attn_fwd_plan(8, 32, 1, 32768, 128, BF16, ctypes.byref(n)) == OK
+    assert lib.attn_fwd_plan(8, 32, 1, 32768, 128, BF16, 0, ctypes.byref(n)) == OK
     assert n.value > 1
-    need = lib.attn_fwd_workspace_size(8, 32, 1, 32768, 128, BF16)
+    need = lib.attn_fwd_workspace_size(8, 32, 1, 32768, 128, BF16, 0)
     assert need == 8 * 32 * 1 * n.value * (128 + 4) * 4
     assert call(lib, **shape, extra=[None, 0]) == E_WORKSPACE
     assert call(lib, **shape, extra=[A16, need - 1]) == E_WORKSPACE
@@ -125,17 +125,45 @@ def test_plan_and_size_queries(lib):
     # prefill shapes never split and need no workspace
     for shp in ((1, 16, 4096, 4096, 64), (2, 16, 8192, 8192, 128), (32, 12, 512, 512, 64),
                 (1, 2, 256, 256, 64)):
-        assert lib.attn_fwd_plan(*shp, BF16, ctypes.byref(n)) == OK and n.value == 1
-        assert lib.attn_fwd_workspace_size(*shp, BF16) == 0
+        assert lib.attn_fwd_plan(*shp, BF16, 0, ctypes.byref(n)) == OK and n.value == 1
+        assert lib.attn_fwd_workspace_size(*shp, BF16, 0) == 0
     # single query over many keys splits; few keys do not
-    assert lib.attn_fwd_plan(8, 32, 1, 32768, 128, BF16, ctypes.byref(n)) == OK and n.value == 8
-    assert lib.attn_fwd_plan(1, 1, 1, 100, 64, BF16, ctypes.byref(n)) == OK and n.value == 1
+    assert lib.attn_fwd_plan(8, 32, 1, 32768, 128, BF16, 0, ctypes.byref(n)) == OK and n.value == 8
+    assert lib.attn_fwd_plan(1, 1, 1, 100, 64, BF16, 0, ctypes.byref(n)) == OK and n.value == 1
+    # few (batch, head, 128-query tile) workgroups over long keys, 16-bit: the
+    # fused kernel over key ranges, about 256 workgroups in all, at least
+    # 1024 keys per range, at most 64 ranges
+    for shp, want in (((1, 32, 64, 32768, 128), 8), ((2, 32, 128, 16384, 64), 4),
+                      ((1, 16, 128, 65536, 64), 16), ((1, 1, 2, 131072, 64), 64),
+                      ((1, 64, 128, 4096, 128), 4), ((1, 128, 128, 4096, 64), 2),
+                      ((1, 64, 200, 8192, 64), 2), ((1, 1, 7, 5000, 64), 4)):
+        for dt in (BF16, F16):
+            assert lib.attn_fwd_plan(*shp, dt, 0, ctypes.byref(n)) == OK and n.value == want, shp
+        B, H, Sq, Sk, d = shp
+        assert lib.attn_fwd_workspace_size(*shp, BF16, 0) == B * H * Sq * want * (d + 4) * 4
+        # fp32 never splits a prefill shape
+        assert lib.attn_fwd_plan(*shp, F32, 0, ctypes.byref(n)) == OK and n.value == 1
+        assert lib.attn_fwd_workspace_size(*shp, F32, 0) == 0
+    # ... and not when the workgroups fill the compute units or the rows see
+    # fewer than 4096 keys
+    for shp in ((1, 256, 128, 8192, 64), (1, 128, 128, 2048, 128), (1, 4, 2000, 4000, 64)):
+        assert lib.attn_fwd_plan(*shp, BF16, 0, ctypes.byref(n)) == OK and n.value == 1, shp
+    # causal rows see at most Sq keys
+    assert lib.attn_fwd_plan(1, 8, 2048, 8192, 128, BF16, 0, ctypes.byref(n)) == OK and n.value == 2
+    assert lib.attn_fwd_plan(1, 8, 2048, 8192, 128, BF16, 1, ctypes.byref(n)) == OK and n.value == 1
+    assert lib.attn_fwd_workspace_size(1, 8, 2048, 8192, 128, BF16, 1) == 0
+    assert lib.attn_fwd_plan(1, 2, 8192, 8192, 64, BF16, 1, ctypes.byref(n)) == OK and n.value == 2
+    assert lib.attn_fwd_plan(8, 32, 1, 32768, 128, BF16, 1, ctypes.byref(n)) == OK and n.value == 1
+    # the fused kernel over key ranges runs one fixed variant
+    t = ctypes.c_int(-1)
+    assert lib.attn_fwd_tile_choice(1, 32, 64, 32768, 128, BF16, 0, ctypes.byref(t)) == OK and t.value == 3
+    assert lib.attn_fwd_tile_choice(2, 32, 128, 16384, 64, F16, 0, ctypes.byref(t)) == OK and t.value == 3
     # rejected arguments
-    assert lib.attn_fwd_plan(0, 1, 1, 1, 64, BF16, ctypes.byref(n)) == E_SHAPE
-    assert lib.attn_fwd_plan(1, 1, 1, 1, 80, BF16, ctypes.byref(n)) == E_UNSUPPORTED
-    assert lib.attn_fwd_plan(1, 1, 1, 1, 64, 7, ctypes.byref(n)) == E_UNSUPPORTED
-    assert lib.attn_fwd_plan(1, 1, 1, 1, 64, BF16, None) == E_NULLPTR
-    assert lib.attn_fwd_workspace_size(0, 1, 1, 1, 64, BF16) == 0
+    assert lib.attn_fwd_plan(0, 1, 1, 1, 64, BF16, 0, ctypes.byref(n)) == E_SHAPE
+    assert lib.attn_fwd_plan(1, 1, 1, 1, 80, BF16, 0, ctypes.byref(n)) == E_UNSUPPORTED
+    assert lib.attn_fwd_plan(1, 1, 1, 1, 64, 7, 0, ctypes.byref(n)) == E_UNSUPPORTED
+    assert lib.attn_fwd_plan(1, 1, 1, 1, 64, BF16, 0, None) == E_NULLPTR
+    assert lib.attn_fwd_workspace_size(0, 1, 1, 1, 64, BF16, 0) == 0
     assert lib.attn_splitk_workspace_size(1, 1, 1, 64, 0) == 0
     assert lib.attn_naive_scratch_size(1, 1, 1, 1, 9) == 0
 
@@ -179,6 +207,9 @@ def test_python_binding_rejects_host_tensors(lib):
     with pytest.raises(ValueError):
         sdpa.attn_fwd(q, q, q)
     assert sdpa.attn_fwd_plan(8, 32, 1, 32768, 128, torch.bfloat16) == 8
+    assert sdpa.attn_fwd_plan(1, 8, 2048, 8192, 128, torch.bfloat16) == 2
+    assert sdpa.attn_fwd_plan(1, 8, 2048, 8192, 128, torch.bfloat16, causal=True) == 1
+    assert sdpa.attn_fwd_workspace_size(1, 8, 2048, 8192, 128, torch.bfloat16) == 8 * 2048 * 2 * 132 * 4
     with pytest.raises(sdpa.AttnError) as ei:
         sdpa.attn_fwd_plan(1, 1, 1, 1, 96, torch.bfloat16)
     assert ei.value.status == E_UNSUPPORTED
@@ -249,9 +280,10 @@ def test_tile_table_entries():
         assert all(0 <= x < N_TILES[d] for x in vals)
 
 
-def tiled(lib, tile=0, q=A16, k=A16, v=A16, o=A16_2, dtype=BF16, d=64, scale=0.125):
-    return lib.attn_fwd_tiled(q, k, v, o, None, 1, 2, 8, 8, d, scale, 0, BHSD, dtype, None, tile,
-                              None)
+def tiled(lib, tile=0, q=A16, k=A16, v=A16, o=A16_2, dtype=BF16, d=64, scale=0.125, n_split=1,
+          ws=None, ws_bytes=0, B=1, H=2, Sq=8, Sk=8):
+    return lib.attn_fwd_tiled(q, k, v, o, None, B, H, Sq, Sk, d, scale, 0, BHSD, dtype, None, tile,
+                              n_split, ws, ws_bytes, None)
 
 
 def test_tiled_validation(lib):
@@ -262,6 +294,19 @@ def test_tiled_validation(lib):
     assert tiled(lib, d=96) == E_UNSUPPORTED
     assert tiled(lib, o=A16 + 8) == E_ALIGN
     assert tiled(lib, scale=-1.0) == E_ARG
+    # key splits: n_split >= 1, 16-bit types only, a workspace of the
+    # split-K size (rows * n_split * (d + 4) floats), 16-byte aligned
+    need = lib.attn_splitk_workspace_size(1, 2, 8, 64, 4)
+    assert need == 2 * 8 * 4 * 68 * 4
+    assert tiled(lib, n_split=0) == E_ARG
+    assert tiled(lib, n_split=-3) == E_ARG
+    assert tiled(lib, n_split=4, dtype=F32, ws=A16, ws_bytes=need) == E_UNSUPPORTED
+    assert tiled(lib, n_split=4) == E_WORKSPACE
+    assert tiled(lib, n_split=4, ws=A16, ws_bytes=need - 1) == E_WORKSPACE
+    assert tiled(lib, n_split=4, ws=A16 + 8, ws_bytes=need) == E_ALIGN
+    # record indices past int32, and key-range ends past int32
+    assert tiled(lib, n_split=1 << 20, B=1, H=64, Sq=64, ws=A16, ws_bytes=1 << 62) == E_SHAPE
+    assert tiled(lib, n_split=1 << 20, Sq=2, Sk=(1 << 31) - 64, H=1, ws=A16, ws_bytes=1 << 62) == E_SHAPE
 
 
 def test_binding_buffer_checks():

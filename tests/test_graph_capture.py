@@ -15,17 +15,22 @@ from scaled_dot_product_flashattention_amd.inputs import WORKLOADS, generate
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["medium_bf16", "decode_bf16"])
+SHAPES = {"medium_bf16": dict(H=4, Sq=512, Sk=512),
+          "decode_bf16": dict(B=2, H=8, Sk=8192),
+          "key_ranges": dict(H=2, Sq=256, Sk=8192)}  # the fused kernel over key ranges
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
 def test_graph_replay_matches_eager(name):
-    base = WORKLOADS[name]
-    w = base.replace(H=4, Sq=512, Sk=512) if name == "medium_bf16" else base.replace(B=2, H=8, Sk=8192)
+    base = WORKLOADS["medium_bf16" if name == "key_ranges" else name]
+    w = base.replace(**SHAPES[name])
     inputs = [generate(w, seed=s) for s in (31, 32, 33)]
     dev = torch.device("cuda:0")
     q, k, v = (inputs[0][n].to(dev) for n in ("q", "k", "v"))
     B, H, Sq, Sk, d = w.B, w.H, w.Sq, w.Sk, w.d
-    n_split = sdpa.attn_fwd_plan(B, H, Sq, Sk, d, q.dtype)
+    n_split = sdpa.attn_fwd_plan(B, H, Sq, Sk, d, q.dtype, w.causal)
     say(f"graph capture {name}: B{B} H{H} Sq{Sq} Sk{Sk} d{d} n_split={n_split}")
-    ws = torch.empty(max(sdpa.attn_fwd_workspace_size(B, H, Sq, Sk, d, q.dtype), 16), dtype=torch.uint8,
+    ws = torch.empty(max(sdpa.attn_fwd_workspace_size(B, H, Sq, Sk, d, q.dtype, w.causal), 16), dtype=torch.uint8,
                      device=dev)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
