@@ -22,9 +22,12 @@ def library_path() -> str:
 def compile_source(source: str, out: str, extra: list[str] | None = None) -> str:
     """Compile one C source into a shared library at ``out``."""
     cc = os.environ.get("CC", "gcc")
-    cmd = [cc, *CFLAGS, *(extra or []), source, "-o", out + ".tmp", "-lm"]
+    # a temporary name per process: concurrent builds (parallel test workers)
+    # each replace the library atomically with a complete file
+    tmp = f"{out}.tmp{os.getpid()}"
+    cmd = [cc, *CFLAGS, *(extra or []), source, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(out + ".tmp", out)
+    os.replace(tmp, out)
     return out
 
 
