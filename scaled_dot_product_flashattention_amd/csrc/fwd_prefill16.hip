@@ -135,13 +135,15 @@ __device__ __forceinline__ bool sum_out_of_range(float l) {
 //   NST    LDS ring stages (NST - 2 tiles in flight ahead)
 //   KSPLIT 1: 4 waves, each over all keys of a tile; 2: 8 waves, wave w
 //          takes key half w / 4 of every tile for the queries of wave w % 4
+//   OCC    waves per SIMD the registers are sized for (two; three for a
+//          lean tile whose workgroups share a compute unit three at a time)
 //   SPLIT  each workgroup takes one range of p.chunk keys and, instead of
 //          O and LSE, writes per query row the record (m, l, -, -, o[D]) of
 //          its range: the reference max m (log2 units; -inf when l = 0), the
 //          sum l against it and the unnormalised output o. The records of
 //          the ranges of a row combine exactly by the block rule.
-template <typename Tag, int D, int NQ, int BN, int NST, int KSPLIT, bool SPLIT>
-__global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel(Prefill16Params p) {
+template <typename Tag, int D, int NQ, int BN, int NST, int KSPLIT, int OCC, bool SPLIT>
+__global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kernel(Prefill16Params p) {
     constexpr int NT = 256 * KSPLIT;               // threads
     constexpr int KBW = BN / 32 / KSPLIT;          // 32-key blocks per wave and tile
     constexpr int RB = D * 2;                      // bytes per K/V row
@@ -625,7 +627,7 @@ __global__ __launch_bounds__(256 * KSPLIT, 2 / KSPLIT) void fwd_prefill16_kernel
     }
 }
 
-template <typename Tag, int D, int NQ, int BN, int NST, int KSPLIT, bool SPLIT>
+template <typename Tag, int D, int NQ, int BN, int NST, int KSPLIT, int OCC, bool SPLIT>
 hipError_t launch16(const FwdArgs& a, hipStream_t stream) {
     constexpr int BM = 4 * 32 * NQ;
     Prefill16Params p;
@@ -653,7 +655,7 @@ hipError_t launch16(const FwdArgs& a, hipStream_t stream) {
     const int64_t grid = (int64_t)p.n_qtiles * a.B * a.H * p.n_split;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     p.remap = (grid % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((fwd_prefill16_kernel<Tag, D, NQ, BN, NST, KSPLIT, SPLIT>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((fwd_prefill16_kernel<Tag, D, NQ, BN, NST, KSPLIT, OCC, SPLIT>), dim3((unsigned)grid),
                        dim3(256 * KSPLIT), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !SPLIT) return e;
@@ -662,28 +664,29 @@ hipError_t launch16(const FwdArgs& a, hipStream_t stream) {
 
 // ---- tile variants and their choice ----------------------------------------
 // Tile sizes are not probed at run time: the candidates below are compiled in
-// (each without register spills at two waves per SIMD), and a table made
+// (each without register spills at its waves per SIMD), and a table made
 // offline by timing every candidate over a grid of shapes (tile_table.inc)
 // names the variant per head size, masking, key length and query rows.
 struct Variant16 {
     int nq, bn, nst, ksplit, lds;
     hipError_t (*run[2][2])(const FwdArgs&, hipStream_t);  // [whole keys, key splits][fp16, bf16]
 };
-#define ATTN_VARIANT16(D, NQ, BN, NST, KS)                                                   \
-    {NQ, BN, NST, KS, lds_bytes16(D, NQ, BN, NST, KS),                                       \
-     {{&launch16<F16, D, NQ, BN, NST, KS, false>, &launch16<BF16, D, NQ, BN, NST, KS, false>}, \
-      {&launch16<F16, D, NQ, BN, NST, KS, true>, &launch16<BF16, D, NQ, BN, NST, KS, true>}}}
+#define ATTN_VARIANT16(D, NQ, BN, NST, KS, OCC)                                                        \
+    {NQ, BN, NST, KS, lds_bytes16(D, NQ, BN, NST, KS),                                                  \
+     {{&launch16<F16, D, NQ, BN, NST, KS, OCC, false>, &launch16<BF16, D, NQ, BN, NST, KS, OCC, false>}, \
+      {&launch16<F16, D, NQ, BN, NST, KS, OCC, true>, &launch16<BF16, D, NQ, BN, NST, KS, OCC, true>}}}
 const Variant16 kVariants64[] = {
-    ATTN_VARIANT16(64, 1, 64, 5, 1),  // 0: 128 queries x 64 keys, 4 waves
-    ATTN_VARIANT16(64, 1, 64, 4, 1),  // 1: same, shorter ring
-    ATTN_VARIANT16(64, 2, 64, 8, 2),  // 2: 256 queries, 8 waves in two key halves
-    ATTN_VARIANT16(64, 1, 64, 8, 2),  // 3: 128 queries, 8 waves in two key halves
+    ATTN_VARIANT16(64, 1, 64, 5, 1, 2),  // 0: 128 queries x 64 keys, 4 waves
+    ATTN_VARIANT16(64, 1, 64, 4, 1, 2),  // 1: same, shorter ring
+    ATTN_VARIANT16(64, 2, 64, 8, 2, 2),  // 2: 256 queries, 8 waves in two key halves
+    ATTN_VARIANT16(64, 1, 64, 8, 2, 2),  // 3: 128 queries, 8 waves in two key halves
+    ATTN_VARIANT16(64, 1, 32, 4, 1, 3),  // 4: 128 queries x 32 keys, 4 waves, three per SIMD
 };
 const Variant16 kVariants128[] = {
-    ATTN_VARIANT16(128, 1, 32, 5, 1),  // 0: 128 queries x 32 keys, 4 waves
-    ATTN_VARIANT16(128, 1, 32, 4, 1),  // 1: same, shorter ring
-    ATTN_VARIANT16(128, 1, 64, 4, 2),  // 2: 128 queries x 64 keys, 8 waves in two key halves
-    ATTN_VARIANT16(128, 1, 64, 5, 2),  // 3: same, deeper ring (all 160 KiB of LDS)
+    ATTN_VARIANT16(128, 1, 32, 5, 1, 2),  // 0: 128 queries x 32 keys, 4 waves
+    ATTN_VARIANT16(128, 1, 32, 4, 1, 2),  // 1: same, shorter ring
+    ATTN_VARIANT16(128, 1, 64, 4, 2, 2),  // 2: 128 queries x 64 keys, 8 waves in two key halves
+    ATTN_VARIANT16(128, 1, 64, 5, 2, 2),  // 3: same, deeper ring (all 160 KiB of LDS)
 };
 #undef ATTN_VARIANT16
 constexpr int kNumVariants64 = sizeof(kVariants64) / sizeof(kVariants64[0]);
