@@ -298,7 +298,7 @@ const char* attn_status_string(int status) {
     case ATTN_E_ALIGN: return "misaligned pointer (tensors and workspaces 16 bytes, lse and kv_len 4 bytes)";
     case ATTN_E_WORKSPACE: return "workspace or scratch missing or too small";
     case ATTN_E_HIP: return "the HIP runtime reported an error at launch";
-    case ATTN_E_ARG: return "scale must be finite and >= 0";
+    case ATTN_E_ARG: return "invalid argument: scale negative, NaN or infinite, tile variant out of range, or n_split < 1";
     default: return "unknown status";
     }
 }
