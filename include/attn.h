@@ -102,7 +102,8 @@ size_t attn_fwd_workspace_size(int B, int H, int Sq, int Sk, int d, int dtype, i
  * splits). More, with two or more queries per head (fp16/bf16 only): the
  * fused kernel over key ranges, used when its (batch, head, 128-query tile)
  * workgroups number fewer than 256 and a row sees at least 4096 keys, with
- * about 256 workgroups in all and at least 1024 keys per range.
+ * about 512 workgroups in all, at least 1024 keys per range and at most 64
+ * ranges.
  * Host only; returns a status and writes *n_split on success. */
 int attn_fwd_plan(int B, int H, int Sq, int Sk, int d, int dtype, int causal, int* n_split);
 

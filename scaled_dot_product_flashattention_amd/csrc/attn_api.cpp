@@ -30,8 +30,13 @@ constexpr int kSplitMinKeys = 512;       // keys per split, at least
 // Key splits of the fused 16-bit kernel, for two or more queries per head:
 // when its (batch, head, 128-query tile) workgroups would not fill the
 // compute units and the keys are long, each workgroup takes one key range
-// and the merge kernel combines the ranges' records.
-constexpr int kFusedSplitTargetGroups = 256;  // split below this many workgroups, up to about this many
+// and the merge kernel combines the ranges' records. The ranges run the
+// 4-wave 128-query variant, two workgroups per compute unit; about 512
+// workgroups in all was the fastest count on every few-head shape measured
+// on MI355X (8 to 16 ranges at 32 to 128 query tiles over 16384 to 32768
+// keys, 9-14 % faster than about 256 with the 8-wave variant).
+constexpr int kFusedSplitBelow = 256;         // split when fewer workgroups than this
+constexpr int kFusedSplitTargetGroups = 512;  // up to about this many workgroups
 constexpr int kFusedSplitMinKeys = 1024;      // keys per range, at least
 constexpr int kFusedSplitMinTotal = 4096;     // keys per row, at least, to split at all
 constexpr int kFusedSplitMax = 64;            // ranges, at most
@@ -75,7 +80,7 @@ int check_call(const void* q, const void* k, const void* v, const void* o, const
 int plan_fused_splits(int B, int H, int Sq, int Sk, int dtype) {
     if (dtype == ATTN_F32 || Sk < kFusedSplitMinTotal) return 1;
     const int64_t groups = (int64_t)B * H * ((Sq + 127) / 128);
-    if (groups >= kFusedSplitTargetGroups) return 1;
+    if (groups >= kFusedSplitBelow) return 1;
     int64_t n = (kFusedSplitTargetGroups + groups - 1) / groups;
     if (n > Sk / kFusedSplitMinKeys) n = Sk / kFusedSplitMinKeys;
     if (n > kFusedSplitMax) n = kFusedSplitMax;

@@ -650,8 +650,9 @@ hipError_t launch16(const FwdArgs& a, hipStream_t stream) {
     p.n_qtiles = (a.Sq + BM - 1) / BM;
     p.ws = static_cast<float*>(a.ws);
     p.n_split = SPLIT ? a.n_split : 1;
-    // whole tiles per key range
-    p.chunk = SPLIT ? (a.Sk + a.n_split * BN - 1) / (a.n_split * BN) * BN : a.Sk;
+    // key ranges of whole 64-key blocks (whole tiles of every variant)
+    static_assert(64 % BN == 0, "key ranges must be whole tiles");
+    p.chunk = SPLIT ? (a.Sk + a.n_split * 64 - 1) / (a.n_split * 64) * 64 : a.Sk;
     const int64_t grid = (int64_t)p.n_qtiles * a.B * a.H * p.n_split;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     p.remap = (grid % 8 == 0) ? 1 : 0;
@@ -694,13 +695,12 @@ constexpr int kNumVariants128 = sizeof(kVariants128) / sizeof(kVariants128[0]);
 
 #include "tile_table.inc"
 
-// With key ranges the grid holds about one workgroup per compute unit, and
-// each workgroup waits on its loads more than on its arithmetic: the variant
-// with eight waves (two key halves of 64-key tiles, 128 queries) was the
-// fastest, or within a few percent of it, on every few-head shape measured
-// on gfx950 (32 to 128 query tiles over 4096 to 65536 keys, both head sizes).
-constexpr int kRangeTile64 = 3;
-constexpr int kRangeTile128 = 3;
+// With key ranges the grid holds about two workgroups per compute unit: the
+// 4-wave, 128-query variant with the 4-stage ring was the fastest on every
+// few-head shape measured on gfx950 (32 to 128 query tiles over 4096 to
+// 32768 keys, both head sizes), ahead of the 8-wave ones at half the ranges.
+constexpr int kRangeTile64 = 1;
+constexpr int kRangeTile128 = 1;
 static_assert(kRangeTile64 < kNumVariants64 && kRangeTile128 < kNumVariants128, "key-range variant");
 
 // Bucket of x on a log2 grid starting at 2^lo with n points (nearest point).

@@ -131,12 +131,12 @@ def test_plan_and_size_queries(lib):
     assert lib.attn_fwd_plan(8, 32, 1, 32768, 128, BF16, 0, ctypes.byref(n)) == OK and n.value == 8
     assert lib.attn_fwd_plan(1, 1, 1, 100, 64, BF16, 0, ctypes.byref(n)) == OK and n.value == 1
     # few (batch, head, 128-query tile) workgroups over long keys, 16-bit: the
-    # fused kernel over key ranges, about 256 workgroups in all, at least
+    # fused kernel over key ranges, about 512 workgroups in all, at least
     # 1024 keys per range, at most 64 ranges
-    for shp, want in (((1, 32, 64, 32768, 128), 8), ((2, 32, 128, 16384, 64), 4),
-                      ((1, 16, 128, 65536, 64), 16), ((1, 1, 2, 131072, 64), 64),
-                      ((1, 64, 128, 4096, 128), 4), ((1, 128, 128, 4096, 64), 2),
-                      ((1, 64, 200, 8192, 64), 2), ((1, 1, 7, 5000, 64), 4)):
+    for shp, want in (((1, 32, 64, 32768, 128), 16), ((2, 32, 128, 16384, 64), 8),
+                      ((1, 16, 128, 65536, 64), 32), ((1, 1, 2, 131072, 64), 64),
+                      ((1, 64, 128, 4096, 128), 4), ((1, 128, 128, 4096, 64), 4),
+                      ((1, 64, 200, 8192, 64), 4), ((1, 1, 7, 5000, 64), 4)):
         for dt in (BF16, F16):
             assert lib.attn_fwd_plan(*shp, dt, 0, ctypes.byref(n)) == OK and n.value == want, shp
         B, H, Sq, Sk, d = shp
@@ -149,15 +149,15 @@ def test_plan_and_size_queries(lib):
     for shp in ((1, 256, 128, 8192, 64), (1, 128, 128, 2048, 128), (1, 4, 2000, 4000, 64)):
         assert lib.attn_fwd_plan(*shp, BF16, 0, ctypes.byref(n)) == OK and n.value == 1, shp
     # causal rows see at most Sq keys
-    assert lib.attn_fwd_plan(1, 8, 2048, 8192, 128, BF16, 0, ctypes.byref(n)) == OK and n.value == 2
+    assert lib.attn_fwd_plan(1, 8, 2048, 8192, 128, BF16, 0, ctypes.byref(n)) == OK and n.value == 4
     assert lib.attn_fwd_plan(1, 8, 2048, 8192, 128, BF16, 1, ctypes.byref(n)) == OK and n.value == 1
     assert lib.attn_fwd_workspace_size(1, 8, 2048, 8192, 128, BF16, 1) == 0
-    assert lib.attn_fwd_plan(1, 2, 8192, 8192, 64, BF16, 1, ctypes.byref(n)) == OK and n.value == 2
+    assert lib.attn_fwd_plan(1, 2, 8192, 8192, 64, BF16, 1, ctypes.byref(n)) == OK and n.value == 4
     assert lib.attn_fwd_plan(8, 32, 1, 32768, 128, BF16, 1, ctypes.byref(n)) == OK and n.value == 1
     # the fused kernel over key ranges runs one fixed variant
     t = ctypes.c_int(-1)
-    assert lib.attn_fwd_tile_choice(1, 32, 64, 32768, 128, BF16, 0, ctypes.byref(t)) == OK and t.value == 3
-    assert lib.attn_fwd_tile_choice(2, 32, 128, 16384, 64, F16, 0, ctypes.byref(t)) == OK and t.value == 3
+    assert lib.attn_fwd_tile_choice(1, 32, 64, 32768, 128, BF16, 0, ctypes.byref(t)) == OK and t.value == 1
+    assert lib.attn_fwd_tile_choice(2, 32, 128, 16384, 64, F16, 0, ctypes.byref(t)) == OK and t.value == 1
     # rejected arguments
     assert lib.attn_fwd_plan(0, 1, 1, 1, 64, BF16, 0, ctypes.byref(n)) == E_SHAPE
     assert lib.attn_fwd_plan(1, 1, 1, 1, 80, BF16, 0, ctypes.byref(n)) == E_UNSUPPORTED
@@ -207,9 +207,9 @@ def test_python_binding_rejects_host_tensors(lib):
     with pytest.raises(ValueError):
         sdpa.attn_fwd(q, q, q)
     assert sdpa.attn_fwd_plan(8, 32, 1, 32768, 128, torch.bfloat16) == 8
-    assert sdpa.attn_fwd_plan(1, 8, 2048, 8192, 128, torch.bfloat16) == 2
+    assert sdpa.attn_fwd_plan(1, 8, 2048, 8192, 128, torch.bfloat16) == 4
     assert sdpa.attn_fwd_plan(1, 8, 2048, 8192, 128, torch.bfloat16, causal=True) == 1
-    assert sdpa.attn_fwd_workspace_size(1, 8, 2048, 8192, 128, torch.bfloat16) == 8 * 2048 * 2 * 132 * 4
+    assert sdpa.attn_fwd_workspace_size(1, 8, 2048, 8192, 128, torch.bfloat16) == 8 * 2048 * 4 * 132 * 4
     with pytest.raises(sdpa.AttnError) as ei:
         sdpa.attn_fwd_plan(1, 1, 1, 1, 96, torch.bfloat16)
     assert ei.value.status == E_UNSUPPORTED
