@@ -38,7 +38,8 @@
 //     [2^-100, 2^32], which for typical scores happens on a row's first tiles
 //     at most. Any common reference gives the same softmax.
 //   * Workgroups of one head stay on one XCD (its L2 then serves every re-read
-//     of that head's K/V); causal tiles start longest-first.
+//     of that head's K/V); causal tiles start longest-first, across all the
+//     heads of an XCD.
 #include "device_common.h"
 #include "launch.h"
 
@@ -73,6 +74,10 @@ struct Prefill16Params {
     int causal;
     int n_qtiles;
     int remap;  // grid size is a multiple of 8: keep each head's tiles on one XCD
+    // causal mask with B*H a multiple of 8 (key ranges excluded) and the K/V
+    // of one XCD's heads within kCausalMixBytes: those B*H/8 heads take
+    // turns, query tile by query tile (0: head by head)
+    int causal_heads;
     // key splits (SPLIT kernels): workgroup split s takes keys
     // [s * chunk, (s + 1) * chunk) and writes its (m, l, o) records to ws
     float* ws;
@@ -184,6 +189,15 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     const int G = gridDim.x;
     const int g = blockIdx.x;
     int w = p.remap ? (g & 7) * (G >> 3) + (g >> 3) : g;
+    if (p.causal_heads) {
+        // XCD x (workgroups g = x mod 8) still takes the heads of its range,
+        // but in the order (query tile, head): with the reversal below, the
+        // longest tiles of all its heads go first. Head by head, a late
+        // head's longest tile would start last and end the kernel.
+        const int j = g >> 3;
+        const int qrank = j / p.causal_heads;
+        w = (g & 7) * (G >> 3) + (j - qrank * p.causal_heads) * p.n_qtiles + qrank;
+    }
     // query tiles innermost: the tiles of one key range of a head run
     // together and share its K/V in L2
     int split = 0;
@@ -627,6 +641,14 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     }
 }
 
+// Causal tiles of all the heads of an XCD interleaved (longest first) while
+// those heads' K and V take at most this many bytes: measured on gfx950, the
+// interleave cut 11-24 % at 4-8 MiB (B4 H16 S2048, B8 H16 S1024, B2 H32 S4096,
+// head size 64) and gained nothing at 16 MiB (B2 H16 S8192, head size 128),
+// where the competing heads' K/V no longer fit the XCD's 4 MiB L2 and the
+// HBM reads grew 1.75x.
+constexpr int64_t kCausalMixBytes = int64_t(8) << 20;
+
 template <typename Tag, int D, int NQ, int BN, int NST, int KSPLIT, int OCC, bool SPLIT>
 hipError_t launch16(const FwdArgs& a, hipStream_t stream) {
     constexpr int BM = 4 * 32 * NQ;
@@ -656,6 +678,9 @@ hipError_t launch16(const FwdArgs& a, hipStream_t stream) {
     const int64_t grid = (int64_t)p.n_qtiles * a.B * a.H * p.n_split;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     p.remap = (grid % 8 == 0) ? 1 : 0;
+    const int64_t bh = (int64_t)a.B * a.H;
+    const int64_t xcd_kv_bytes = bh / 8 * (int64_t)a.Sk * D * 2 * 2;
+    p.causal_heads = (a.causal && !SPLIT && bh % 8 == 0 && xcd_kv_bytes <= kCausalMixBytes) ? (int)(bh / 8) : 0;
     hipLaunchKernelGGL((fwd_prefill16_kernel<Tag, D, NQ, BN, NST, KSPLIT, OCC, SPLIT>), dim3((unsigned)grid),
                        dim3(256 * KSPLIT), 0, stream, p);
     hipError_t e = hipGetLastError();

@@ -148,3 +148,19 @@ def test_binding_rejects_bad_buffers():
         sdpa.attn_softmax_rows(q.view(-1, 64), lse=torch.empty(5, device="cuda"))
     with pytest.raises(ValueError):
         sdpa.attn_softmax_rows(q.view(-1, 64), mode="two_pass")
+
+
+# Causal grids with B*H a multiple of 8 and small K/V: the fused kernel runs
+# the query tiles of each XCD's heads interleaved, longest first, in place of
+# head by head. Every tile variant, ragged query tiles, Sq != Sk.
+CAUSAL_MIX = [(d, t, shape) for d, n in ((64, 5), (128, 4)) for t in range(n)
+              for shape in ((2, 4, 700, 700, "bhsd", "bf16"), (1, 8, 300, 900, "bshd", "f16"))]
+
+
+@pytest.mark.parametrize("d,tile,shape", CAUSAL_MIX)
+def test_causal_interleaved_heads(d, tile, shape):
+    B, H, Sq, Sk, layout, dtype = shape
+    w = W["long_causal_bf16"].replace(name=f"causal_mix_{B}x{H}_{Sq}_{Sk}_d{d}_t{tile}", B=B, H=H,
+                                      Sq=Sq, Sk=Sk, d=d, layout=layout, dtype=dtype,
+                                      seed=4000 + 10 * d + tile)
+    full_case(w, path=f"tile:{tile}:1")
