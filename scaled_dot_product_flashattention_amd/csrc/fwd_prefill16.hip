@@ -157,7 +157,10 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     constexpr int STAGE_B = 2 * TILE_B;            // K tile, then V tile
     constexpr int DMA1 = TILE_B / 16 / NT;         // DMA loads per thread, tensor and tile
     constexpr int DPT = 2 * DMA1;                  // ... for K and V
-    constexpr int P = NST - 2;                     // tiles issued ahead
+    // Rings of 6 or more stages take one barrier per two tiles (at even t),
+    // which costs one stage of lookahead.
+    constexpr bool BAR2 = NST >= 6;
+    constexpr int P = BAR2 ? NST - 3 : NST - 2;    // tiles issued ahead
     constexpr int OROW = D + 8;                    // output staging row (elements)
     constexpr int MRG_W = (NQ * (D / 32) * 16 + 2 * NQ) * 64 * 4;  // one wave's (O, m, l) in fp32
     constexpr int LDS_B = lds_bytes16(D, NQ, BN, NST, KSPLIT);
@@ -168,6 +171,7 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     static_assert(KBW >= 1 && BN % (32 * KSPLIT) == 0, "key tile must split over the wave groups");
     static_assert(DMA1 >= 1 && TILE_B % (16 * NT) == 0, "tile must split over the lanes");
     static_assert(P >= 2, "the pipeline needs two tiles in flight");
+    static_assert(!BAR2 || P >= 3, "tile t+2 must be issued before the barrier of t");
     static_assert((P - 2) * DPT < 64, "vmcnt range");
     using T = uint16_t;
     using SAcc = f32x16[KBW][NQ];
@@ -440,7 +444,8 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     // ---- the key loop ---------------------------------------------------------
     // Iteration t (tile t's probabilities): wait for tile t+1, barrier, issue
     // the DMA of tile t+P into the stage of tile t-2 (its last reads completed
-    // before the products of iteration t-1), read K(t+1); mask tile t's scores
+    // before the products of iteration t-1) -- with BAR2, at even t only, for
+    // tiles t+1, t+2 and into the stages of t-3, t-2 --, read K(t+1); mask tile t's scores
     // where some row cannot see all its keys; then the products P(t-1) V(t-1)
     // and K(t+1) Q^T, one at a time, each followed by its share of tile t's
     // probabilities; check the sums; read V(t) for the next iteration.
@@ -452,9 +457,21 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
         SAcc& s_nxt = s_buf[B ^ 1];
         PAcc& p_cur = pq[B];
         PAcc& p_prv = pq[B ^ 1];
-        if (t + 1 < ntiles) wait_tile(t + 1, min(t + P - 1, ntiles - 1));
-        barrier_nofence();
-        if (t + P < ntiles) issue_tile(t + P);
+        if constexpr (BAR2) {
+            // even t only: tiles t+1 and t+2 (read in iterations t and t+1)
+            // have landed for every wave; after the barrier every wave is past
+            // iteration t-1, so the stages of tiles t-3 and t-2 are free
+            if constexpr (B == 0) {
+                if (t + 1 < ntiles) wait_tile(min(t + 2, ntiles - 1), min(t + P - 1, ntiles - 1));
+                barrier_nofence();
+                if (t + P < ntiles) issue_tile(t + P);
+                if (t + P + 1 < ntiles) issue_tile(t + P + 1);
+            }
+        } else {
+            if (t + 1 < ntiles) wait_tile(t + 1, min(t + P - 1, ntiles - 1));
+            barrier_nofence();
+            if (t + P < ntiles) issue_tile(t + P);
+        }
         const unsigned char* kt = stage(t + 1);
         const unsigned char* vt = stage(t > 0 ? t - 1 : 0);
         if (wkey0(t) + KBW * 32 > wave_lim_min) mask_scores(s_cur, t);
@@ -515,6 +532,7 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
 #pragma unroll
             for (int kb = 0; kb < KBW; ++kb) pq[1][gq][kb][0] = pq[1][gq][kb][1] = u32x4{0u, 0u, 0u, 0u};
     }
+    // register set 0 serves the even tiles (the BAR2 barrier relies on it)
     int t = 0;
     for (; t + 1 < ntiles; t += 2) {
         iteration(int_c<0>{}, t);
