@@ -73,3 +73,15 @@ def test_table_choice_is_the_default_path():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(o1, o3)
     assert torch.equal(l1, l2) and torch.equal(l1, l3)
+
+
+# Key walks of exactly 1 .. 6 tiles (and a ragged last tile): the pipeline's
+# ends, and with rings of 8 stages the barrier taken at even tiles only.
+WALKS = [(d, t, sk) for d in (64, 128) for t in range(N_TILES[d]) for sk in (64, 128, 191, 256, 320, 383)]
+
+
+@pytest.mark.parametrize("d,tile,Sk", WALKS)
+def test_short_key_walks(d, tile, Sk):
+    w = W["medium_bf16"].replace(name=f"walk_{Sk}_d{d}_t{tile}", B=1, H=2, Sq=300, Sk=Sk, d=d,
+                                 seed=900 + Sk + tile)
+    full_case(w, path=f"tile:{tile}")
