@@ -21,11 +21,14 @@
 //     softmax of key tile t, the same wave issues the matrix products of
 //     P(t-1) V(t-1) and K(t+1) Q^T, one product between every few
 //     probabilities. On gfx950 a wave's own vector instructions issue while
-//     its matrix product runs; those of another wave on the same SIMD wait
-//     for the matrix unit, so the overlap has to come from within the wave.
+//     its matrix product runs. Two wave groups in opposite, barrier-separated
+//     phases (one multiplying while the other computes probabilities) were
+//     measured much slower, so the overlap is arranged within the wave.
 //   * K and V tiles travel global -> LDS by direct DMA loads
 //     (global_load_lds_dwordx4) into an NST-stage ring, NST-2 tiles ahead of
-//     the tile whose keys are multiplied; no registers are spent on staging.
+//     the tile whose keys are multiplied (NST-3 for rings of 6 or more
+//     stages, which pass one barrier per two tiles); no registers are spent
+//     on staging.
 //     Both sit in LDS row-major with their 16-byte chunks XOR-swizzled per
 //     row so that the K operand reads (ds_read_b128) and the transposing V
 //     operand reads (ds_read_b64_tr_b16) are free of bank conflicts.
@@ -39,7 +42,7 @@
 //     at most. Any common reference gives the same softmax.
 //   * Workgroups of one head stay on one XCD (its L2 then serves every re-read
 //     of that head's K/V); causal tiles start longest-first, across all the
-//     heads of an XCD.
+//     heads of an XCD when their K/V are small enough to share its L2.
 #include "device_common.h"
 #include "launch.h"
 
