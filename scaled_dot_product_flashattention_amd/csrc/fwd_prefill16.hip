@@ -35,11 +35,14 @@
 //   * KSPLIT = 2: two groups of 4 waves take the two key halves of every
 //     tile for the same queries (each key operand then feeds two query
 //     blocks), and merge their (m, l, O) through LDS at the end.
-//   * The running max is a reference: probabilities are taken against it
-//     directly and only the row sum is checked. The exact max (with the
-//     rescale of l and O) is computed only when a sum leaves
-//     [2^-100, 2^32], which for typical scores happens on a row's first tiles
-//     at most. Any common reference gives the same softmax.
+//   * The running max is a reference: it starts at the exact maximum of
+//     each row over the wave's first key tile, and later probabilities are
+//     taken against it directly; only the row sum is checked. The exact max
+//     (with the rescale of l and O) is taken again only when a lane's sum
+//     passes 2^32 (or a 16-bit probability overflows), i.e. when a later
+//     tile's scores rise far above the first tile's. Any common reference
+//     gives the same softmax; starting at a row's own maximum keeps its
+//     largest probabilities at 1 or more, in the normal range of fp16.
 //   * Workgroups of one head stay on one XCD (its L2 then serves every re-read
 //     of that head's K/V); causal tiles start longest-first, across all the
 //     heads of an XCD when their K/V are small enough to share its L2.
@@ -51,10 +54,11 @@ namespace attn {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
-// The reference max stays while every lane's running sum lies in
-// [2^-100, 2^32] (bit patterns below): probabilities then neither overflow
-// nor lose precision to underflow.
-constexpr uint32_t kSumLoBits = 0x0D800000u;  // 2^-100
+// The reference max stays while every lane's running sum is at most 2^32
+// (bit pattern below). The reference starts at the row's maximum over its
+// first tile, so each row's sum is at least 1 from then on and nothing of
+// weight underflows; a lane whose own keys all sit far below the maximum may
+// hold a tiny or zero sum, which is harmless.
 constexpr uint32_t kSumHiBits = 0x4F800000u;  // 2^32
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -131,9 +135,10 @@ __device__ __forceinline__ void barrier_nofence() {
     asm volatile("" ::: "memory");
 }
 
-// True where a running sum left [2^-100, 2^32] (or is not a number).
+// True where a running sum (never negative) passed 2^32, is infinite (a
+// 16-bit probability overflowed) or is not a number.
 __device__ __forceinline__ bool sum_out_of_range(float l) {
-    return (__float_as_uint(l) - kSumLoBits) > (kSumHiBits - kSumLoBits);
+    return __float_as_uint(l) > kSumHiBits;
 }
 
 // Template parameters:
@@ -395,10 +400,9 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
                     if (wkey0(tile) + kb * 32 + blk_row(r, hh) >= lim) S[kb][gq][r] = kNegInf;
         }
     };
-    // Block gq after a sum left the range: move the reference to the exact
-    // running max, rescale l (O by the caller, with the returned factor) and
-    // redo the probabilities. Both lane halves of a query decide alike.
-    auto exact_max = [&](int gq, const SAcc& S, PAcc& Pm) __attribute__((always_inline)) -> float {
+    // Maximum of query block gq's scores in S over both lane halves (the
+    // whole row of the tile), in log2 units; -inf when every key is masked.
+    auto row_max = [&](int gq, const SAcc& S) __attribute__((always_inline)) -> float {
         float mq[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
         for (int kb = 0; kb < KBW; ++kb)
@@ -410,7 +414,13 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
             }
         float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
         mx = fmaxf(mx, swap_halves(mx));
-        const float mxs = mx * c;  // -inf stays -inf (c > 0)
+        return mx * c;  // -inf stays -inf (c > 0)
+    };
+    // Block gq after a sum left the range: move the reference to the exact
+    // running max, rescale l (O by the caller, with the returned factor) and
+    // redo the probabilities. Both lane halves of a query decide alike.
+    auto exact_max = [&](int gq, const SAcc& S, PAcc& Pm) __attribute__((always_inline)) -> float {
+        const float mxs = row_max(gq, S);
         const float l_row_old = l_old[gq] + swap_halves(l_old[gq]);
         // nothing accumulated yet: the old reference carries no weight
         float m_new = l_row_old > 0.f ? fmaxf(m_run[gq], mxs) : mxs;
@@ -530,6 +540,16 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
 #pragma unroll
         for (int i = 0; i < NQK; ++i) qk_mfma(i, s_buf[0]);
         read_v_carry(0);
+        // The reference of each row starts at its exact maximum over this
+        // wave's first tile. Masks only grow with the key index, so a row
+        // with no valid key in that tile has none in the wave's later tiles
+        // either; its reference stays 0 and its sum 0.
+        if (wkey0(0) + KBW * 32 > wave_lim_min) mask_scores(s_buf[0], 0);
+#pragma unroll
+        for (int gq = 0; gq < NQ; ++gq) {
+            const float mx = row_max(gq, s_buf[0]);
+            m_run[gq] = mx == kNegInf ? 0.f : mx;
+        }
 #pragma unroll
         for (int gq = 0; gq < NQ; ++gq)
 #pragma unroll

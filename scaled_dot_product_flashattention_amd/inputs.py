@@ -12,6 +12,12 @@ distributions beyond the shapes):
   2.0 to widen the score spread);
 * per-sequence key lengths ``rng.integers(lo, hi + 1, size=B)`` when the
   workload pads keys;
+* optionally a score offset: column 0 of q is set to 8 and column 0 of key j
+  to o_j / (8 * scale), so that every row's scaled scores gain o_j, which
+  runs linearly from ``score_shift[0]`` at the first key to
+  ``score_shift[1]`` at the last (natural-log units; softmax ignores a
+  common offset, so this probes the kernels' handling of very low or rising
+  scores);
 * a round-to-nearest-even cast to the storage dtype with torch ``.to``.
 
 The oracle and the GPU path read exactly these quantised tensors.
@@ -40,6 +46,8 @@ class Workload:
     causal: bool = False
     qk_mult: float = 1.0  # multiplier applied to q and k before the cast
     kv_len_range: tuple[int, int] | None = None  # inclusive range of valid key counts
+    # offset of the scaled scores at the first and the last key (see above)
+    score_shift: tuple[float, float] | None = None
     seed: int = 0
     description: str = ""
 
@@ -98,7 +106,24 @@ def generate(w: Workload, seed: int | None = None) -> dict:
         out["kv_len"] = torch.from_numpy(rng.integers(lo, hi + 1, size=w.B).astype(np.int32))
     else:
         out["kv_len"] = None
+    if w.score_shift is not None:
+        _shift_scores(out["q"], out["k"], w)
     return out
+
+
+def _key_axis(layout: str) -> int:
+    return 1 if layout == "bshd" else 2
+
+
+def _shift_scores(q: torch.Tensor, k: torch.Tensor, w: Workload) -> None:
+    """Column 0 of q := 8 and column 0 of key j := o_j / (8 * scale), in place
+    (o_j linear from score_shift[0] to score_shift[1] over the keys)."""
+    lo, hi = w.score_shift
+    ramp = np.linspace(lo, hi, w.Sk, dtype=np.float64) / (8.0 * w.scale)
+    shape = [1] * k.dim()
+    shape[_key_axis(w.layout)] = w.Sk
+    q[..., 0] = 8.0
+    k[..., 0] = torch.from_numpy(ramp.astype(np.float32)).reshape(shape[:-1]).to(k.dtype)
 
 
 def generate_periodic_keys(w: Workload, period: int, seed: int | None = None) -> dict:

@@ -7,15 +7,15 @@ rule. Every tile variant runs on shapes that exercise the edges of the
 ranges: ranges past the valid keys (empty records), more ranges than key
 tiles, causal rows that see no key of a range, key padding with
 NaN-poisoned rows past kv_len (kv_len 0 included), large scores that move
-the reference max, scale 0, the fp16 probability window, and the
-head-group layout. attn_fwd must take the same path, bit for bit, where its
-plan splits, and the full-size few-head shapes are checked on sampled rows.
+the reference max, scale 0, the fp16 probability window, rows shifted far
+below zero, and the head-group layout. attn_fwd must take the same path, bit for bit, where its
+plan splits, and the full-size few-head shapes are checked on every row.
 Bar: 2e-2 max-abs on O and LSE. Runs on an MI355X only."""
 import pytest
 import torch
 
 import scaled_dot_product_flashattention_amd as sdpa
-from parity_util import full_case, sampled_case, say
+from parity_util import full_case, full_size_case, say
 from scaled_dot_product_flashattention_amd.inputs import WORKLOADS, generate
 
 pytestmark = pytest.mark.gpu
@@ -37,7 +37,16 @@ SHAPES = {
     # q, k x 4: the ranges' reference maxima differ widely
     "large_scores": (1, 2, 64, 4000, False, (2000, 4000), "bhsd", 6, {"qk_mult": 4.0}),
     "scale_zero": (2, 2, 65, 1500, True, (1, 1500), "bshd", 3, {"scale": 0.0}),
-    "fp16_overflow_window": (1, 2, 100, 3000, False, None, "bhsd", 4, {"scale": 0.69}),
+    "wide_spread": (1, 2, 100, 3000, False, None, "bhsd", 4, {"scale": 0.69}),
+    # every score shifted by -8 .. -20 (natural log): each range's reference
+    # starts at its own first tile's maximum
+    "shift_m8": (1, 2, 100, 3000, False, None, "bhsd", 4, {"score_shift": (-8.0, -8.0)}),
+    "shift_m14": (1, 2, 130, 2500, True, None, "bshd", 4, {"score_shift": (-14.0, -14.0)}),
+    "shift_m20": (2, 2, 100, 3000, False, (1, 3000), "bhsd", 5, {"score_shift": (-20.0, -20.0)}),
+    # scores rising by 12 (fp16 probabilities overflow inside a range) and
+    # falling by 20 over the keys (the ranges' maxima differ by 20)
+    "fp16_overflow_window": (1, 2, 100, 3000, False, None, "bhsd", 4, {"score_shift": (0.0, 12.0)}),
+    "falling_scores": (1, 2, 100, 3000, False, None, "bhsd", 4, {"score_shift": (0.0, -20.0)}),
     "two_queries": (1, 3, 2, 5000, False, (1, 5000), "bhsd", 8, {}),
 }
 
@@ -88,4 +97,4 @@ def test_planned_split_full_size(name):
     n = sdpa.attn_fwd_plan(w.B, w.H, w.Sq, w.Sk, w.d, dt, w.causal)
     say(f"{name}: plan {n} key ranges")
     assert n > 1
-    sampled_case(w, path="fused", n_rows=40)
+    full_size_case(w, path="fused", poison=w.kv_len_range is not None)

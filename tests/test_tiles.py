@@ -4,13 +4,14 @@ The tuned table may send any shape to any variant, so each variant is held
 to the same bar as the default path (2e-2 max-abs for 16-bit inputs) on
 shapes that exercise its edges: a single partial tile, ragged query and key
 tails, causal masks with Sq != Sk, key padding with NaN-poisoned rows past
-kv_len, the head-group layout, and the full medium and long-causal sizes on
-sampled rows. Runs on an MI355X only."""
+kv_len, the head-group layout, rows whose scores all sit far below zero or
+rise or fall steeply over the keys, and the full workload sizes. Runs on an
+MI355X only."""
 import pytest
 import torch
 
 import scaled_dot_product_flashattention_amd as sdpa
-from parity_util import full_case, sampled_case, say
+from parity_util import full_case, full_size_case, say
 from scaled_dot_product_flashattention_amd.inputs import WORKLOADS, generate
 
 pytestmark = pytest.mark.gpu
@@ -31,10 +32,24 @@ SHAPES = {  # name: (B, H, Sq, Sk, causal, kv_len range, layout, extra workload 
     "scale_above_one": (1, 2, 300, 700, False, None, "bhsd", {"scale": 2.0}),
     # scale * log2(e) ~ 1 on large scores
     "scale_at_one": (1, 2, 300, 700, False, None, "bhsd", {"scale": 0.69, "qk_mult": 2.0}),
-    # row maxima 15..30 above the reference (base 2): the running sum stays
-    # inside its range, but fp16 probabilities overflow 65504; the infinite
-    # row sum sends the tile to the exact-maximum path
-    "fp16_overflow_window": (1, 2, 300, 700, False, None, "bhsd", {"scale": 0.69}),
+    # wide score spread (about 8 in log2 units): later tiles' maxima sit
+    # above the first tile's, which sets the reference
+    "wide_spread": (1, 2, 300, 700, False, None, "bhsd", {"scale": 0.69}),
+    # every score of a row shifted by -8 .. -20 (natural log): softmax is
+    # unchanged; fp16 probabilities against a reference far above the row's
+    # maximum would fall into the subnormal range
+    "shift_m8": (1, 2, 300, 700, False, None, "bhsd", {"score_shift": (-8.0, -8.0)}),
+    "shift_m14": (1, 2, 300, 700, True, None, "bshd", {"score_shift": (-14.0, -14.0)}),
+    "shift_m17": (2, 2, 300, 700, False, (300, 700), "bhsd", {"score_shift": (-17.0, -17.0)}),
+    "shift_m20": (1, 2, 300, 700, False, None, "bhsd", {"score_shift": (-20.0, -20.0)}),
+    # scores falling by 20 over the keys: the first tile holds the maxima
+    "falling_scores": (1, 2, 300, 700, False, None, "bhsd", {"score_shift": (0.0, -20.0)}),
+    # scores rising by 12 over the keys: later fp16 probabilities pass 65504
+    # against the first tile's reference while the sums stay below 2^32; the
+    # infinite sum sends the tile to the exact-maximum path
+    "fp16_overflow_window": (1, 2, 300, 700, False, None, "bhsd", {"score_shift": (0.0, 12.0)}),
+    # scores rising by 30: the sums pass 2^32 for both types
+    "rising_scores": (1, 2, 300, 700, True, (400, 700), "bshd", {"score_shift": (0.0, 30.0)}),
     # scale 0 (uniform weights over the valid keys), with causal rows and padding
     "scale_zero": (2, 2, 200, 333, True, (1, 333), "bshd", {"scale": 0.0}),
 }
@@ -54,9 +69,11 @@ def test_tile_variant_matches_oracle(dtype, d, tile, shape):
 
 @pytest.mark.parametrize("name,tile", [(n, t) for n in ("medium_bf16", "long_causal_bf16", "bert_pad_fp16")
                                        for t in range(N_TILES[WORKLOADS[n].d])])
+@pytest.mark.timeout(900)
 def test_tile_variant_full_size(name, tile):
-    """Each variant at a full workload size, on sampled rows."""
-    sampled_case(W[name], path=f"tile:{tile}", n_rows=32)
+    """Each variant at a full workload size, every row (the oracle's result
+    is computed once per workload and shared by its variants)."""
+    full_size_case(W[name], path=f"tile:{tile}", poison=W[name].kv_len_range is not None)
 
 
 def test_table_choice_is_the_default_path():
