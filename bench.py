@@ -31,8 +31,27 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def flops(w) -> float:
+    """Nominal FLOPs of one forward: 4*B*H*Sq*Sk*d, halved for causal masks."""
     f = 4.0 * w.B * w.H * w.Sq * w.Sk * w.d
     return f / 2 if w.causal else f
+
+
+def valid_pairs(w, kv_len) -> float:
+    """(query, key) pairs the method computes: keys below each sequence's
+    length and, with a causal mask, keys j <= i."""
+    import numpy as np
+
+    lens = np.full(w.B, w.Sk, dtype=np.int64) if kv_len is None else \
+        np.clip(np.asarray(kv_len, dtype=np.int64), 0, w.Sk)
+    i = np.arange(w.Sq, dtype=np.int64)
+    tot = sum(int(np.minimum(i + 1, n).sum()) if w.causal else w.Sq * int(n) for n in lens)
+    return float(tot) * w.H
+
+
+def algorithmic_flops(w, kv_len) -> float:
+    """FLOPs credited to a step: the nominal count, except for key padding,
+    where only the valid pairs count (4*d FLOPs each)."""
+    return 4.0 * w.d * valid_pairs(w, kv_len) if w.kv_len_range is not None else flops(w)
 
 
 def kv_bytes(w) -> float:
@@ -57,11 +76,30 @@ def stored_traffic(workload: str, path: str, kind: str):
 
 
 def cpu_share() -> int:
-    try:
-        n = len(os.sched_getaffinity(0))
-    except AttributeError:  # pragma: no cover
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    """Host threads for the oracle: OMP_NUM_THREADS where the machine sets it
+    (a shared GPU machine allots its CPUs per GPU and says so there), else every
+    CPU this process may run on."""
+    import oracle
+
+    return oracle.host_threads()
+
+
+def output_rows(o, rows, w):
+    """Rows (b*H + h)*Sq + i of the output o (any layout) as a float64 array."""
+    import numpy as np
+
+    o_c = o.float().cpu()
+    out = np.empty((len(rows), w.d))
+    for n, r in enumerate(rows):
+        i, h, b = r % w.Sq, (r // w.Sq) % w.H, r // (w.Sq * w.H)
+        if w.layout == "bhsd":
+            out[n] = o_c[b, h, i].numpy()
+        elif w.layout == "bshd":
+            out[n] = o_c[b, i, h].numpy()
+        else:
+            g = o_c.shape[3]
+            out[n] = o_c[b, h // g, i, h % g].numpy()
+    return out
 
 
 def timed_region(step, steps: int, stream, torch):
@@ -100,9 +138,11 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(w, t, target_s: float = 12.0):
+def cpu_baseline(w, t, o=None, lse=None, target_s: float = 12.0):
     """The fp64 oracle on a bounded sample of rows of the same workload,
-    timed on the host cores, scaled to the metric's unit."""
+    timed on the host cores, scaled to the metric's unit. With the GPU's
+    output (o, lse) of the same inputs, also the largest differences on
+    those rows."""
     import numpy as np
 
     import oracle
@@ -114,21 +154,32 @@ def cpu_baseline(w, t, target_s: float = 12.0):
     while True:
         rows = np.sort(rng.choice(R, size=n, replace=False))
         t0 = time.perf_counter()
-        oracle.attention_rows(t["q"], t["k"], t["v"], rows, scale=w.scale, causal=w.causal,
-                              layout=w.layout, kv_len=t["kv_len"], nthreads=cores)
+        o_ref, lse_ref = oracle.attention_rows(t["q"], t["k"], t["v"], rows, scale=w.scale,
+                                               causal=w.causal, layout=w.layout,
+                                               kv_len=t["kv_len"], nthreads=cores)
         dt = time.perf_counter() - t0
         if dt >= target_s / 4 or n >= R:
             break
         n = min(R, max(n * 2, int(n * target_s / max(dt, 1e-3))))
-    if w.causal:
-        i = rows % w.Sq
-        f = float(np.sum(4.0 * w.d * np.minimum(i + 1, w.Sk)))
-    else:
-        f = 4.0 * w.d * w.Sk * len(rows)
-    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "cpu_model": cpu_model(),
-            "sample": f"{len(rows)} of {R} query rows of the same workload, full key range each, "
-                      f"{dt:.1f} s wall on {cores} threads (fp64, three-step softmax)"}
+    # the pairs of the sampled rows
+    lens = np.full(w.B, w.Sk) if t["kv_len"] is None else np.clip(t["kv_len"].numpy(), 0, w.Sk)
+    i, b = rows % w.Sq, rows // (w.Sq * w.H)
+    f = float(np.sum(4.0 * w.d * (np.minimum(i + 1, lens[b]) if w.causal else lens[b])))
+    rec = {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+           "cpu_model": cpu_model(), "host_cpus_visible": os.cpu_count(),
+           "wall_s": round(dt, 2), "gflops": round(f / dt / 1e9, 2),
+           "full_workload_s_estimate": round(dt * valid_pairs(w, t["kv_len"]) * 4.0 * w.d / f, 1),
+           "sample": f"{len(rows)} of {R} query rows of the same workload, full key range each, "
+                     f"{dt:.1f} s wall on {cores} threads (fp64, three-step softmax)"}
+    if o is not None:
+        got = output_rows(o, rows, w)
+        got_l = lse.cpu().numpy().reshape(-1)[rows].astype(np.float64)
+        both_inf = np.isneginf(got_l) & np.isneginf(lse_ref)
+        with np.errstate(invalid="ignore"):
+            dl = np.where(both_inf, 0.0, np.abs(got_l - lse_ref))
+        rec["gpu_max_abs_err"] = {"o": float(np.abs(got - o_ref).max()), "lse": float(dl.max()),
+                                  "rows": len(rows)}
+    return rec
 
 
 def bench_softmax(args, w, torch, sdpa) -> int:
@@ -256,6 +307,8 @@ def main() -> int:
                     help="override the workload's tensor layout: bhsd ([B,H,S,d]), bshd "
                          "([B,S,H,d]) or split:g ([B,H/g,S,g,d], heads in groups of g)")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-clock", action="store_true",
+                    help="do not sample the GFX clock (amdsmi) over an extra 0.4 s of steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run 3 plain device copies of 256 MiB so a "
                          "counter profile of this run can scale its byte counters")
@@ -338,6 +391,18 @@ def main() -> int:
     wall_ms = (time.perf_counter() - t_wall) * 1e3
 
     peak_bytes = torch.cuda.max_memory_allocated(dev)
+    clock = None
+    if not args.skip_clock:
+        from scaled_dot_product_flashattention_amd.profiling import gfx_clock_during
+
+        n_clk = max(1, int(400.0 / max(ms, 1e-3)))
+
+        def run_clk():
+            for _ in range(n_clk):
+                step()
+            torch.cuda.synchronize()
+        clock = gfx_clock_during(run_clk)
+        clock["steps"] = n_clk
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -346,7 +411,8 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    fl = flops(w)
+    fl_nominal = flops(w)
+    fl = algorithmic_flops(w, t["kv_len"])
     # the split-over-keys kernels run for one query per head
     splitk_kernels = args.path == "splitk" or (n_split > 1 and Sq == 1)
     # below the ridge (peak FLOP/s over peak bytes/s) the K/V stream bounds
@@ -364,6 +430,11 @@ def main() -> int:
         peak = PEAK_TFLOPS_F32 if w.dtype == "f32" else PEAK_TFLOPS_16
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(tflops / peak, 4)}
+        if clock and "mhz_median" in clock:
+            # the matrix peak scales with the shader clock (spec: 2400 MHz)
+            peak_clk = peak * clock["mhz_median"] / 2400.0
+            roof["peak_at_measured_clock"] = round(peak_clk, 1)
+            roof["frac_at_measured_clock"] = round(tflops / peak_clk, 4)
         if args.config == "medium_bf16" and args.path == "fused" and not relaid:
             metric = "fused attention fwd TFLOP/s and % bf16 MFMA peak, B1 H16 S4096 d64"
         else:
@@ -391,13 +462,18 @@ def main() -> int:
         "config": {"workload": w.name, "description": w.description, "B": B, "H": H, "Sq": Sq,
                    "Sk": Sk, "d": d, "layout": w.layout, "causal": w.causal, "path": args.path,
                    "graph": args.graph,
-                   "n_split": n_split, "tile": tile, "flops_per_step": fl, "wall_ms_timed_region": round(wall_ms, 2),
+                   "n_split": n_split, "tile": tile, "flops_per_step": fl,
+                   "flops_nominal": fl_nominal,
+                   "flops_counted": "valid (query, key) pairs x 4d" if w.kv_len_range is not None
+                   else "4*B*H*Sq*Sk*d" + (", halved (causal)" if w.causal else ""),
+                   "wall_ms_timed_region": round(wall_ms, 2),
                    "peak_device_bytes": peak_bytes},
         "timing": timing_summary(ms, batches),
         "roofline": roof,
+        "gfx_clock": clock,
     }
     if not args.skip_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, t)
+        line["cpu_baseline"] = cpu_baseline(w, t, o, lse)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -55,6 +55,19 @@ def layout_shape(layout: str, B: int, H: int, S: int, d: int) -> tuple:
     g = layout_code(layout) & 0xffff
     return (B, H // g, S, g, d)
 
+def host_threads() -> int:
+    """Threads the oracle uses by default: OMP_NUM_THREADS when set (a shared
+    machine sets it to the CPUs it allots to the job), else every CPU this
+    process may run on."""
+    env = os.environ.get("OMP_NUM_THREADS", "").strip()
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
 _c_i64 = ctypes.c_int64
 _c_int = ctypes.c_int
 _c_dbl = ctypes.c_double
@@ -162,7 +175,7 @@ class Oracle:
 
     @staticmethod
     def _threads(nthreads):
-        return int(nthreads) if nthreads else (os.cpu_count() or 1)
+        return int(nthreads) if nthreads else host_threads()
 
     # -- entry points --------------------------------------------------------
     def attention(self, q, k, v, *, scale=None, causal=False, layout="bhsd", kv_len=None,

@@ -169,6 +169,80 @@ def write_traffic(fetch_db: str, write_db: str, kernel: str, workload: str, path
     return rec
 
 
+def gfx_clock_during(run, device_index: int = 0, period_s: float = 0.002):
+    """Sample the GFX (shader) clock of the GPU with amdsmi while ``run()``
+    executes (``run`` should keep the GPU busy for a fraction of a second and
+    return once the work is done). Returns {"mhz_median", "mhz_min",
+    "mhz_max", "samples", "source"}, or {"error": ...} when amdsmi or its
+    clock readings are unavailable; ``run`` is called in every case.
+
+    The reading is the firmware's current GFX clock: the mean over XCDs of
+    the gpu-metrics table's per-XCD clocks where the table has them, else the
+    clock-info query."""
+    import threading
+    import time
+
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception as e:  # noqa: BLE001 - any failure means "no clock"
+        run()
+        return {"error": f"amdsmi unavailable: {type(e).__name__}: {e}"}
+    try:
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if not handles:
+            run()
+            return {"error": "amdsmi lists no GPU"}
+        h = handles[min(device_index, len(handles) - 1)]
+
+        def read():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                xs = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and c > 0]
+                if xs:
+                    return sum(xs) / len(xs), "gpu_metrics current_gfxclks (mean over XCDs)"
+                c = m.get("current_gfxclk")
+                if isinstance(c, int) and c > 0:
+                    return float(c), "gpu_metrics current_gfxclk"
+            except Exception:  # noqa: BLE001
+                pass
+            c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX).get("clk")
+            return (float(c), "clock_info GFX") if isinstance(c, int) and c > 0 else (None, "")
+
+        samples: list[float] = []
+        source = [""]
+        stop = threading.Event()
+
+        def sampler():
+            while not stop.is_set():
+                try:
+                    v, src = read()
+                except Exception:  # noqa: BLE001
+                    v, src = None, ""
+                if v is not None:
+                    samples.append(v)
+                    source[0] = src
+                time.sleep(period_s)
+
+        th = threading.Thread(target=sampler, daemon=True)
+        th.start()
+        try:
+            run()
+        finally:
+            stop.set()
+            th.join()
+        if not samples:
+            return {"error": "no clock samples"}
+        srt = sorted(samples)
+        return {"mhz_median": srt[len(srt) // 2], "mhz_min": srt[0], "mhz_max": srt[-1],
+                "samples": len(srt), "source": source[0]}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:  # noqa: BLE001
+            pass
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)

@@ -11,6 +11,7 @@ Tolerances (the study's stated bar):
 from __future__ import annotations
 
 import sys
+import time
 
 import numpy as np
 import torch
@@ -92,47 +93,41 @@ def full_case(w: Workload, path="fused", n_split=None, poison=False, seed=None, 
     return check(w, oe, le, o_ref, lse_ref, f"{w.name}/{path}")
 
 
-def sampled_rows(w: Workload, n: int, rng) -> np.ndarray:
-    """Rows (b*H + h)*Sq + i to check at full size: first and last rows, tile
-    edges, the ragged end, and random picks."""
-    R = w.B * w.H * w.Sq
-    picks = {0, R - 1, w.Sq - 1, min(w.Sq, 127), min(w.Sq - 1, 128), (w.B - 1) * w.H * w.Sq}
-    picks |= set(rng.choice(R, size=min(n, R), replace=False).tolist())
-    return np.array(sorted(p for p in picks if 0 <= p < R), dtype=np.int64)
+# The oracle's whole results for the last few full-size workloads, kept for
+# later calls on the same inputs (the paths and tile variants of a workload
+# share one): (workload, seed, poison) -> (inputs, O, LSE), oldest first.
+# The five workloads' entries take about 6 GB of host memory together.
+_FULL_CACHE: dict = {}
+_FULL_CACHE_MAX = 6
 
 
-def sampled_case(w: Workload, path="fused", n_rows=48, n_split=None, seed=None):
-    """Full-size run on the GPU; the oracle recomputes sampled rows."""
-    say(f"case {w.name} full size {path} B{w.B} H{w.H} Sq{w.Sq} Sk{w.Sk} d{w.d} {w.dtype} "
-        f"{w.layout} causal={w.causal}")
-    t = generate(w, seed)
+def full_size_case(w: Workload, path="fused", n_split=None, seed=None, poison=False):
+    """Full-size run on the GPU against every row of the oracle's output."""
+    say(f"case {w.name} full size {path} n_split={n_split} B{w.B} H{w.H} Sq{w.Sq} Sk{w.Sk} d{w.d} "
+        f"{w.dtype} {w.layout} causal={w.causal} pad={w.kv_len_range}")
+    key = (w, seed, poison)
+    hit = _FULL_CACHE.get(key)
+    if hit is None:
+        while len(_FULL_CACHE) >= _FULL_CACHE_MAX:
+            del _FULL_CACHE[next(iter(_FULL_CACHE))]
+        t = generate(w, seed)
+        if poison:
+            poison_padding(t["k"], t["v"], t["kv_len"], w.layout)
+        t0 = time.perf_counter()
+        o_ref, lse_ref = oracle.attention(t["q"], t["k"], t["v"], scale=w.scale, causal=w.causal,
+                                          layout=w.layout, kv_len=t["kv_len"])
+        say(f"  oracle over all {w.B * w.H * w.Sq} rows: {time.perf_counter() - t0:.1f} s")
+        hit = _FULL_CACHE[key] = (t, o_ref, lse_ref)
+    t, o_ref, lse_ref = hit
     q, k, v, kl = (to_dev(t[n]) for n in ("q", "k", "v", "kv_len"))
     o, lse = run_path(path, q, k, v, w, kl, n_split)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(1234)
-    rows = sampled_rows(w, n_rows, rng)
-    o_ref, lse_ref = oracle.attention_rows(t["q"], t["k"], t["v"], rows, scale=w.scale,
-                                           causal=w.causal, layout=w.layout, kv_len=t["kv_len"])
-    o_c = o.float().cpu()
-    lse_c = lse.cpu().numpy().astype(np.float64)
-    got = np.empty_like(o_ref)
-    got_l = np.empty_like(lse_ref)
-    for n, r in enumerate(rows):
-        i, h, b = r % w.Sq, (r // w.Sq) % w.H, r // (w.Sq * w.H)
-        if w.layout == "bhsd":
-            got[n] = o_c[b, h, i].numpy()
-        elif w.layout == "bshd":
-            got[n] = o_c[b, i, h].numpy()
-        else:
-            g = o_c.shape[3]
-            got[n] = o_c[b, h // g, i, h % g].numpy()
-        got_l[n] = lse_c[b, h, i]
-    both_inf = np.isneginf(got_l) & np.isneginf(lse_ref)
-    with np.errstate(invalid="ignore"):
-        dl = np.where(both_inf, 0.0, np.abs(got_l - lse_ref))
-    res = check(w, np.abs(got - o_ref), dl, o_ref, lse_ref, f"{w.name}/{path}/sampled")
+    del q, k, v
+    oe, le = errors(o, lse, o_ref, lse_ref)
+    res = check(w, oe, le, o_ref, lse_ref, f"{w.name}/{path}/full")
     # properties that hold at any size: finite output, |O| bounded by max|V|
+    o_c = o.float().cpu()
     assert torch.isfinite(o_c).all(), "non-finite output"
-    vmax = float(t["v"].float().abs().max())
+    vmax = float(torch.nan_to_num(t["v"].float(), nan=0.0).abs().max())
     assert float(o_c.abs().max()) <= vmax * (1 + 1e-2) + 1e-6, "|O| exceeds max |V|"
     return res

@@ -59,20 +59,16 @@ def test_qkv_proj_matches_oracle(shape, dtype, layout):
 
 
 @pytest.mark.parametrize("layout", ["bhsd", "bshd"])
-def test_qkv_proj_full_size_sampled(layout):
-    """Medium width at full length (B1 S4096 D1024 H16 d64), checked on a
-    sample of token rows: each output row depends only on its token, so the
-    oracle on those tokens alone is exact for them."""
+def test_qkv_proj_full_size(layout):
+    """Medium width at full length (B1 S4096 D1024 H16 d64), every output
+    element against the oracle."""
     B, S, D, H, d = 1, 4096, 1024, 16, 64
     t = generate_qkv_proj(B, S, D, H, d, "bf16", seed=7)
     got = sdpa.attn_qkv_proj(t["x"].cuda(), t["w"].cuda(), H=H, d=d, layout=layout)
     torch.cuda.synchronize()
-    rows = np.sort(np.random.default_rng(8).choice(S, size=96, replace=False))
-    rows = np.unique(np.concatenate([rows, [0, 127, 128, S - 1]]))
-    want = oracle.qkv_proj(t["x"][:, rows].contiguous(), t["w"], H=H, d=d, layout=layout)
+    want = oracle.qkv_proj(t["x"], t["w"], H=H, d=d, layout=layout)
     for name, g, wnt in zip("qkv", got, want):
-        gs = g[:, :, rows] if layout == "bhsd" else g[:, rows]
-        check(gs, wnt, "bf16", f"{name} rows sample")
+        check(g, wnt, "bf16", f"{name} full")
 
 
 def test_qkv_proj_feeds_attention():

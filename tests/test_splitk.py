@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import scaled_dot_product_flashattention_amd as sdpa
-from parity_util import full_case, sampled_case
+from parity_util import full_case, full_size_case
 from scaled_dot_product_flashattention_amd.inputs import WORKLOADS, generate
 
 pytestmark = pytest.mark.gpu
@@ -48,5 +48,5 @@ def test_split_counts_agree():
         assert float((o - outs[0]).abs().max()) <= 2e-2
 
 
-def test_decode_full_size_sampled():
-    sampled_case(DEC, path="splitk", n_split=8)
+def test_decode_full_size():
+    full_size_case(DEC, path="splitk", n_split=8)
