@@ -64,8 +64,10 @@ enum attn_status {
     ATTN_E_ALIGN = 4,       /* a pointer is not aligned as stated above          */
     ATTN_E_WORKSPACE = 5,   /* workspace / scratch NULL or smaller than required */
     ATTN_E_HIP = 6,         /* the HIP runtime reported an error at launch       */
-    ATTN_E_ARG = 7          /* scale negative, NaN or infinite; tile out of range;
+    ATTN_E_ARG = 7,         /* scale negative, NaN or infinite; tile out of range;
                              * n_split < 1 in attn_fwd_tiled                   */
+    ATTN_E_SCRATCH_LIMIT = 8 /* attn_fwd_noalloc: the plan needs more workspace
+                              * than ATTN_NOALLOC_SCRATCH_BYTES                */
 };
 
 enum attn_layout { ATTN_LAYOUT_BHSD = 0, ATTN_LAYOUT_BSHD = 1 };
@@ -90,6 +92,28 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
              int dtype, const int32_t* kv_len, void* workspace, size_t workspace_bytes,
              void* stream);
+
+/*
+ * attn_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, plan, kernels and results, without the workspace
+ * arguments. Where attn_fwd's plan needs a workspace, this call uses a
+ * static device buffer of the library instead: ATTN_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) per GPU, held from the first such call on that GPU until the
+ * process ends. A plan that needs more (attn_fwd_workspace_size above the
+ * limit) returns ATTN_E_SCRATCH_LIMIT without launching anything. The call
+ * allocates nothing, neither device nor pinned memory; its first call on a
+ * GPU that needs the buffer looks up the buffer's address there (a HIP
+ * symbol query, made with that GPU current) and keeps it.
+ * All calls on one GPU share that buffer: calls whose plans use it and that
+ * may overlap on that GPU (other streams, other threads without ordering)
+ * race and give wrong results. Calls ordered on one stream are safe; no
+ * clearing is needed between them.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
+                     int dtype, const int32_t* kv_len, void* stream);
 
 /* Bytes of workspace attn_fwd needs for this shape (0 when it plans no split).
  * Returns 0 for arguments attn_fwd would reject. Host only. */

@@ -9,6 +9,7 @@ from .api import (  # noqa: F401
     AttnError,
     attn_fwd,
     attn_fwd_naive,
+    attn_fwd_noalloc,
     attn_fwd_plan,
     attn_fwd_splitk,
     attn_fwd_tile_choice,

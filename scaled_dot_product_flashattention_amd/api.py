@@ -93,6 +93,8 @@ def load_library() -> ctypes.CDLL:
     L.attn_fwd_tile_choice.restype = i
     L.attn_fwd_tiled.argtypes = tensors + [i, i, vp, sz, vp]
     L.attn_fwd_tiled.restype = i
+    L.attn_fwd_noalloc.argtypes = tensors + [vp]
+    L.attn_fwd_noalloc.restype = i
     L.attn_status_string.argtypes = [i]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_version.argtypes = []
@@ -257,6 +259,23 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, layout="bhsd", kv_len=None, r
                                  _stream(q, stream))
     if rc:
         raise AttnError("attn_fwd", rc)
+    return o, lse
+
+
+def attn_fwd_noalloc(q, k, v, *, scale=None, causal=False, layout="bhsd", kv_len=None,
+                     return_lse=True, out=None, lse=None, stream=None):
+    """attn_fwd with the library's static workspace in place of a caller's:
+    with ``out`` (and ``lse`` or return_lse=False) given, the call allocates
+    no device memory. Plans needing more than ATTN_NOALLOC_SCRATCH_BYTES of
+    workspace raise AttnError (ATTN_E_SCRATCH_LIMIT). Calls that may overlap
+    on one GPU share that workspace and race."""
+    (B, H, Sq, Sk, d), kv_len, scale, o, lse = _prepare(q, k, v, layout, kv_len, scale, lse,
+                                                        return_lse, out)
+    rc = load_library().attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq,
+                                         Sk, d, scale, int(bool(causal)), layout_code(layout),
+                                         dtype_code(q.dtype), _ptr(kv_len), _stream(q, stream))
+    if rc:
+        raise AttnError("attn_fwd_noalloc", rc)
     return o, lse
 
 

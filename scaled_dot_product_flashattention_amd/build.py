@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["attn_api.cpp", "fwd_prefill.hip", "fwd_prefill16.hip", "fwd_splitk.hip", "naive.hip",
-           "qkv_proj.hip", "softmax_rows.hip"]
+           "qkv_proj.hip", "softmax_rows.hip", "noalloc.hip"]
 ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
 
 

@@ -63,9 +63,12 @@ int check_shape(int B, int H, int Sq, int Sk, int d, int layout, int dtype) {
     return ATTN_OK;
 }
 
-int check_call(const void* q, const void* k, const void* v, const void* o, const float* lse,
-               int B, int H, int Sq, int Sk, int d, float scale, int layout, int dtype,
-               const int32_t* kv_len) {
+}  // namespace
+
+namespace attn {
+int check_fwd_call(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   int B, int H, int Sq, int Sk, int d, float scale, int layout, int dtype,
+                   const int32_t* kv_len) {
     if (!q || !k || !v || !o) return ATTN_E_NULLPTR;
     int rc = check_shape(B, H, Sq, Sk, d, layout, dtype);
     if (rc != ATTN_OK) return rc;
@@ -74,6 +77,11 @@ int check_call(const void* q, const void* k, const void* v, const void* o, const
     if (!aligned(lse, 4) || !aligned(kv_len, 4)) return ATTN_E_ALIGN;
     return ATTN_OK;
 }
+}  // namespace attn
+
+namespace {
+
+using attn::check_fwd_call;
 
 // Key splits for the fused kernel (16-bit types, Sq > kSplitMaxQueries);
 // Sk is the keys a row can see
@@ -153,7 +161,7 @@ int attn_fwd_splitk(const void* q, const void* k, const void* v, void* o, float*
                     int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
                     int dtype, const int32_t* kv_len, int n_split, void* workspace,
                     size_t workspace_bytes, void* stream) {
-    int rc = check_call(q, k, v, o, lse, B, H, Sq, Sk, d, scale, layout, dtype, kv_len);
+    int rc = check_fwd_call(q, k, v, o, lse, B, H, Sq, Sk, d, scale, layout, dtype, kv_len);
     if (rc != ATTN_OK) return rc;
     if (n_split < 1 || (int64_t)B * H * Sq * n_split > INT_MAX) return ATTN_E_SHAPE;
     const size_t need = attn::splitk_workspace_bytes(B, H, Sq, d, n_split);
@@ -167,7 +175,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
              int dtype, const int32_t* kv_len, void* workspace, size_t workspace_bytes,
              void* stream) {
-    int rc = check_call(q, k, v, o, lse, B, H, Sq, Sk, d, scale, layout, dtype, kv_len);
+    int rc = check_fwd_call(q, k, v, o, lse, B, H, Sq, Sk, d, scale, layout, dtype, kv_len);
     if (rc != ATTN_OK) return rc;
     const int n = plan_splits(B, H, Sq, Sk, dtype, causal);
     if (n > 1 && Sq <= kSplitMaxQueries)
@@ -210,7 +218,7 @@ int attn_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
                    int dtype, const int32_t* kv_len, int tile, int n_split, void* workspace,
                    size_t workspace_bytes, void* stream) {
-    int rc = check_call(q, k, v, o, lse, B, H, Sq, Sk, d, scale, layout, dtype, kv_len);
+    int rc = check_fwd_call(q, k, v, o, lse, B, H, Sq, Sk, d, scale, layout, dtype, kv_len);
     if (rc != ATTN_OK) return rc;
     if (tile < -1 || tile >= attn::prefill_tile_count(d, dtype) || n_split < 1) return ATTN_E_ARG;
     if (n_split > 1) {
@@ -238,7 +246,7 @@ int attn_fwd_naive(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int H, int Sq, int Sk, int d, float scale, int causal, int layout,
                    int dtype, const int32_t* kv_len, void* scratch, size_t scratch_bytes,
                    void* stream) {
-    int rc = check_call(q, k, v, o, lse, B, H, Sq, Sk, d, scale, layout, dtype, kv_len);
+    int rc = check_fwd_call(q, k, v, o, lse, B, H, Sq, Sk, d, scale, layout, dtype, kv_len);
     if (rc != ATTN_OK) return rc;
     const size_t need = attn::naive_scratch_bytes(B, H, Sq, Sk, dtype);
     if (!scratch || scratch_bytes < need) return ATTN_E_WORKSPACE;
@@ -304,6 +312,7 @@ const char* attn_status_string(int status) {
     case ATTN_E_WORKSPACE: return "workspace or scratch missing or too small";
     case ATTN_E_HIP: return "the HIP runtime reported an error at launch";
     case ATTN_E_ARG: return "invalid argument: scale negative, NaN or infinite, tile variant out of range, or n_split < 1";
+    case ATTN_E_SCRATCH_LIMIT: return "the call needs more workspace than attn_fwd_noalloc's static buffer holds (ATTN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }

@@ -27,6 +27,11 @@ struct FwdArgs {
     void* ws = nullptr;
 };
 
+// The host-side checks of attn_fwd's arguments (status codes of attn.h).
+int check_fwd_call(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   int B, int H, int Sq, int Sk, int d, float scale, int layout, int dtype,
+                   const int32_t* kv_len);
+
 // Fused single-kernel forward (any shape); 16-bit inputs go to run_prefill16.
 hipError_t run_prefill(const FwdArgs& a, hipStream_t stream);
 hipError_t run_prefill16(const FwdArgs& a, hipStream_t stream);

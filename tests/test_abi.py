@@ -15,7 +15,8 @@ from scaled_dot_product_flashattention_amd import build as attn_build
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
-OK, E_NULLPTR, E_SHAPE, E_UNSUPPORTED, E_ALIGN, E_WORKSPACE, E_HIP, E_ARG = range(8)
+OK, E_NULLPTR, E_SHAPE, E_UNSUPPORTED, E_ALIGN, E_WORKSPACE, E_HIP, E_ARG, E_SCRATCH_LIMIT = range(9)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 BHSD, BSHD = 0, 1
 F32, F16, BF16 = 0, 1, 2
 
@@ -56,7 +57,7 @@ def test_exports_every_declared_symbol(lib):
 def test_version_and_status_strings(lib):
     assert lib.attn_version() >= 10000
     seen = set()
-    for s in range(8):
+    for s in range(9):
         txt = sdpa.attn_status_string(s)
         assert txt and txt not in seen
         seen.add(txt)
@@ -68,12 +69,14 @@ def call(lib, fn="attn_fwd", q=A16, k=A16, v=A16, o=A16_2, lse=None, B=1, H=2, S
     args = [q, k, v, o, lse, B, H, Sq, Sk, d, scale, causal, layout, dtype, kv_len]
     if fn == "attn_fwd_splitk":
         args += extra if extra is not None else [4, None, 0]
+    elif fn == "attn_fwd_noalloc":
+        pass  # no workspace arguments
     else:
         args += extra if extra is not None else [None, 0]
     return getattr(lib, fn)(*args, None)
 
 
-@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_splitk", "attn_fwd_naive"])
+@pytest.mark.parametrize("fn", ["attn_fwd", "attn_fwd_splitk", "attn_fwd_naive", "attn_fwd_noalloc"])
 def test_validation_statuses(lib, fn):
     assert call(lib, fn, q=None) == E_NULLPTR
     assert call(lib, fn, k=None) == E_NULLPTR
@@ -118,6 +121,22 @@ def test_workspace_statuses(lib):
     assert call(lib, "attn_fwd_naive", Sk=100, extra=[None, 0]) == E_WORKSPACE
     assert call(lib, "attn_fwd_naive", Sk=100, extra=[A16, need_n - 1]) == E_WORKSPACE
     assert call(lib, "attn_fwd_naive", Sk=100, extra=[A16 + 8, need_n]) == E_ALIGN
+
+
+def test_noalloc_scratch_limit(lib):
+    """attn_fwd_noalloc refuses, before any HIP call, a plan whose workspace
+    exceeds its static buffer; the size query says how much it would need."""
+    shape = (1024, 32, 1, 32768, 128)
+    need = lib.attn_fwd_workspace_size(*shape, BF16, 0)
+    assert need > NOALLOC_SCRATCH_BYTES
+    B, H, Sq, Sk, d = shape
+    assert call(lib, "attn_fwd_noalloc", B=B, H=H, Sq=Sq, Sk=Sk, d=d) == E_SCRATCH_LIMIT
+    assert "ATTN_NOALLOC_SCRATCH_BYTES" in sdpa.attn_status_string(E_SCRATCH_LIMIT)
+    # the largest decode shape of the study fits
+    assert lib.attn_fwd_workspace_size(8, 32, 1, 32768, 128, BF16, 0) <= NOALLOC_SCRATCH_BYTES
+    # and the header states the limit the library uses
+    text = open(HEADER).read()
+    assert "#define ATTN_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
 
 
 def test_plan_and_size_queries(lib):
