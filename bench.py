@@ -75,6 +75,22 @@ def stored_traffic(workload: str, path: str, kind: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def stored_clock(workload: str, path: str, kind: str):
+    """Shader clock (MHz) under the dominant kernel from the committed
+    GRBM_GUI_ACTIVE profile of this workload, or None when there is none or
+    the kernel's source changed since."""
+    fn = os.path.join(PROFILES, f"{workload}_{path}_clock.json")
+    if not os.path.exists(fn):
+        return None
+    with open(fn) as f:
+        rec = json.load(f)
+    from scaled_dot_product_flashattention_amd.profiling import source_digest
+
+    if rec.get("kernel_source_sha256") != source_digest(kind):
+        return None
+    return rec.get("gfx_mhz")
+
+
 def cpu_share() -> int:
     """Host threads for the oracle: OMP_NUM_THREADS where the machine sets it
     (a shared GPU machine allots its CPUs per GPU and says so there), else every
@@ -119,6 +135,20 @@ def timed_region(step, steps: int, stream, torch):
     total = ev[0].elapsed_time(ev[nb]) / steps
     batches = [ev[i].elapsed_time(ev[i + 1]) / sizes[i] for i in range(nb)]
     return total, batches
+
+
+def prewarm(step, seconds: float, torch) -> int:
+    """Run ``step`` until ``seconds`` of wall time have passed (the GPU's
+    clock ramps up under load over tens of milliseconds; a handful of warmup
+    steps of a 0.1 ms kernel would otherwise time the ramp). Returns the
+    number of steps run."""
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            step()
+        n += 50
+        torch.cuda.synchronize()
+    return n
 
 
 def timing_summary(ms: float, batches) -> dict:
@@ -194,6 +224,7 @@ def bench_softmax(args, w, torch, sdpa) -> int:
     lse = torch.empty((rows,), dtype=torch.float32, device=dev)
     mode = args.path[len("softmax_"):]
     step = lambda: sdpa.attn_softmax_rows(x, scale=w.scale, mode=mode, out=y, lse=lse)  # noqa: E731
+    prewarm(step, args.prewarm_s, torch)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -257,6 +288,7 @@ def bench_qkv(args, w, torch, sdpa) -> int:
                 outs.append(y.transpose(1, 2).contiguous() if w.layout == "bhsd" else y)
             sdpa.attn_fwd(*outs, **akw)
         fl = proj_flops + attn_flops
+    prewarm(step, args.prewarm_s, torch)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -307,8 +339,9 @@ def main() -> int:
                     help="override the workload's tensor layout: bhsd ([B,H,S,d]), bshd "
                          "([B,S,H,d]) or split:g ([B,H/g,S,g,d], heads in groups of g)")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
-    ap.add_argument("--skip-clock", action="store_true",
-                    help="do not sample the GFX clock (amdsmi) over an extra 0.4 s of steps")
+    ap.add_argument("--prewarm-s", type=float, default=0.2,
+                    help="before the warmup steps, run steps for this many seconds so the "
+                         "GPU reaches its sustained clock (0 to skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run 3 plain device copies of 256 MiB so a "
                          "counter profile of this run can scale its byte counters")
@@ -370,6 +403,7 @@ def main() -> int:
                          device=dev)
         step = lambda: sdpa.attn_fwd_naive(q, k, v, scratch=sc, **kw)  # noqa: E731
 
+    prewarm_steps = prewarm(step, args.prewarm_s, torch)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -391,18 +425,6 @@ def main() -> int:
     wall_ms = (time.perf_counter() - t_wall) * 1e3
 
     peak_bytes = torch.cuda.max_memory_allocated(dev)
-    clock = None
-    if not args.skip_clock:
-        from scaled_dot_product_flashattention_amd.profiling import gfx_clock_during
-
-        n_clk = max(1, int(400.0 / max(ms, 1e-3)))
-
-        def run_clk():
-            for _ in range(n_clk):
-                step()
-            torch.cuda.synchronize()
-        clock = gfx_clock_during(run_clk)
-        clock["steps"] = n_clk
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -430,9 +452,13 @@ def main() -> int:
         peak = PEAK_TFLOPS_F32 if w.dtype == "f32" else PEAK_TFLOPS_16
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(tflops / peak, 4)}
-        if clock and "mhz_median" in clock:
+        mhz = None if relaid else stored_clock(args.config, args.path, "splitk" if splitk_kernels
+                                                else args.path)
+        if mhz:
             # the matrix peak scales with the shader clock (spec: 2400 MHz)
-            peak_clk = peak * clock["mhz_median"] / 2400.0
+            peak_clk = peak * mhz / 2400.0
+            roof["clock_mhz"] = round(mhz, 1)
+            roof["clock_source"] = "GRBM_GUI_ACTIVE per dispatch over its duration, committed profile"
             roof["peak_at_measured_clock"] = round(peak_clk, 1)
             roof["frac_at_measured_clock"] = round(tflops / peak_clk, 4)
         if args.config == "medium_bf16" and args.path == "fused" and not relaid:
@@ -470,7 +496,7 @@ def main() -> int:
                    "peak_device_bytes": peak_bytes},
         "timing": timing_summary(ms, batches),
         "roofline": roof,
-        "gfx_clock": clock,
+        "prewarm": {"seconds": args.prewarm_s, "steps": prewarm_steps},
     }
     if not args.skip_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, t, o, lse)

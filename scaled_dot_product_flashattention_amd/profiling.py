@@ -4,6 +4,8 @@ Used to keep the measured figures behind bench.py's roofline under profiles/:
 
 * kernel-trace summary: per kernel, dispatch count and mean / min / max
   duration, from a ``rocprofv3 --kernel-trace --stats`` run;
+* shader clock under one kernel: GRBM_GUI_ACTIVE cycles per dispatch over
+  the dispatch's duration, from a ``rocprofv3 --pmc GRBM_GUI_ACTIVE`` run;
 * HBM traffic: per-dispatch FETCH_SIZE and WRITE_SIZE (KiB) of one kernel from
   two ``rocprofv3 --pmc`` runs, each scaled by what the same counter reads for a
   plain device copy of known size in the same run (bench.py --copy-calibration
@@ -13,6 +15,8 @@ Used to keep the measured figures behind bench.py's roofline under profiles/:
         [--timed STEPS --bench-log LOG]
     python -m scaled_dot_product_flashattention_amd.profiling traffic FETCH_DB WRITE_DB \
         --kernel fwd_prefill_kernel --workload medium_bf16 --path fused --command "..."
+    python -m scaled_dot_product_flashattention_amd.profiling clock GRBM_DB \
+        --kernel fwd_prefill16_kernel --workload medium_bf16 --path fused --command "..."
 """
 from __future__ import annotations
 
@@ -169,78 +173,32 @@ def write_traffic(fetch_db: str, write_db: str, kernel: str, workload: str, path
     return rec
 
 
-def gfx_clock_during(run, device_index: int = 0, period_s: float = 0.002):
-    """Sample the GFX (shader) clock of the GPU with amdsmi while ``run()``
-    executes (``run`` should keep the GPU busy for a fraction of a second and
-    return once the work is done). Returns {"mhz_median", "mhz_min",
-    "mhz_max", "samples", "source"}, or {"error": ...} when amdsmi or its
-    clock readings are unavailable; ``run`` is called in every case.
-
-    The reading is the firmware's current GFX clock: the mean over XCDs of
-    the gpu-metrics table's per-XCD clocks where the table has them, else the
-    clock-info query."""
-    import threading
-    import time
-
-    try:
-        import amdsmi
-        amdsmi.amdsmi_init()
-    except Exception as e:  # noqa: BLE001 - any failure means "no clock"
-        run()
-        return {"error": f"amdsmi unavailable: {type(e).__name__}: {e}"}
-    try:
-        handles = amdsmi.amdsmi_get_processor_handles()
-        if not handles:
-            run()
-            return {"error": "amdsmi lists no GPU"}
-        h = handles[min(device_index, len(handles) - 1)]
-
-        def read():
-            try:
-                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
-                xs = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and c > 0]
-                if xs:
-                    return sum(xs) / len(xs), "gpu_metrics current_gfxclks (mean over XCDs)"
-                c = m.get("current_gfxclk")
-                if isinstance(c, int) and c > 0:
-                    return float(c), "gpu_metrics current_gfxclk"
-            except Exception:  # noqa: BLE001
-                pass
-            c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX).get("clk")
-            return (float(c), "clock_info GFX") if isinstance(c, int) and c > 0 else (None, "")
-
-        samples: list[float] = []
-        source = [""]
-        stop = threading.Event()
-
-        def sampler():
-            while not stop.is_set():
-                try:
-                    v, src = read()
-                except Exception:  # noqa: BLE001
-                    v, src = None, ""
-                if v is not None:
-                    samples.append(v)
-                    source[0] = src
-                time.sleep(period_s)
-
-        th = threading.Thread(target=sampler, daemon=True)
-        th.start()
-        try:
-            run()
-        finally:
-            stop.set()
-            th.join()
-        if not samples:
-            return {"error": "no clock samples"}
-        srt = sorted(samples)
-        return {"mhz_median": srt[len(srt) // 2], "mhz_min": srt[0], "mhz_max": srt[-1],
-                "samples": len(srt), "source": source[0]}
-    finally:
-        try:
-            amdsmi.amdsmi_shut_down()
-        except Exception:  # noqa: BLE001
-            pass
+def write_clock(db_path: str, kernel: str, workload: str, path: str, command: str,
+                xccs: int = 8) -> dict:
+    """Shader clock under the kernel from a ``rocprofv3 --pmc GRBM_GUI_ACTIVE``
+    run: the counter (GPU-busy cycles, summed over the XCCs) per dispatch,
+    divided by the XCC count and by the dispatch's duration."""
+    per = counter_per_kernel(db_path, "GRBM_GUI_ACTIVE")
+    kname, k = _pick(per, kernel)
+    cycles = k["kib"] / xccs  # counter_per_kernel's "kib" is the counter's mean value
+    mhz = cycles / (k["avg_ns"] * 1e-9) / 1e6
+    rec = {"workload": workload, "path": path, "kernel": kname,
+           "kernel_source_sha256": source_digest(kernel_kind(kname)),
+           "grbm_gui_active_per_dispatch": k["kib"], "xccs": xccs,
+           "cycles_per_dispatch": cycles, "avg_ns_under_counters": k["avg_ns"],
+           "dispatches": k["dispatches"], "gfx_mhz": mhz, "command": command}
+    base = os.path.join(PROFILES, f"{workload}_{path}_clock")
+    with open(base + ".json", "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = [f"# Shader clock under the kernel: {workload}, {path} path", "", "Command:", "",
+             "```", command, "```", "", f"Kernel: `{kname[:120]}`", "",
+             "| GRBM_GUI_ACTIVE per dispatch (sum over XCCs) | XCCs | cycles | mean duration | clock |",
+             "|---|---|---|---|---|",
+             f"| {k['kib']:.0f} | {xccs} | {cycles:.0f} | {k['avg_ns'] / 1e3:.2f} us | {mhz:.0f} MHz |",
+             "", f"Kernel source sha256 ({kernel_kind(kname)} kernel files): {rec['kernel_source_sha256']}"]
+    with open(base + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return rec
 
 
 def main() -> None:
@@ -261,6 +219,12 @@ def main() -> None:
     r.add_argument("--workload", required=True)
     r.add_argument("--path", required=True)
     r.add_argument("--command", required=True)
+    c = sub.add_parser("clock")
+    c.add_argument("db")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--workload", required=True)
+    c.add_argument("--path", required=True)
+    c.add_argument("--command", required=True)
     a = ap.parse_args()
     if a.cmd == "trace":
         line = None
@@ -268,6 +232,8 @@ def main() -> None:
             with open(a.bench_log) as f:
                 line = [x for x in f.read().splitlines() if x.startswith("{")][-1]
         write_trace(a.db, a.out, a.command, a.timed, line)
+    elif a.cmd == "clock":
+        print(json.dumps(write_clock(a.db, a.kernel, a.workload, a.path, a.command), indent=1))
     else:
         print(json.dumps(write_traffic(a.fetch_db, a.write_db, a.kernel, a.workload, a.path,
                                        a.command), indent=1))
