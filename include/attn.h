@@ -38,6 +38,13 @@
  * input type (nearest-even) before the second product; the output is rounded
  * once to the input type. fp32 inputs keep every step in fp32.
  *
+ * Inputs must be finite. The kernels are compiled on the assumption that no
+ * NaN occurs (a maximum of a NaN and a number may return either), and a NaN
+ * or infinity in q, k or v inside the valid keys gives an undefined result:
+ * it may poison the whole output row, also where exact arithmetic would give
+ * that key zero weight (0 * inf). Key/value rows past kv_len are never read,
+ * so they may hold anything.
+ *
  * Execution: every call validates all arguments on the host first and
  * returns an error status without touching the GPU when one is bad. On
  * success it enqueues its kernels on `stream` (a hipStream_t; NULL is the
