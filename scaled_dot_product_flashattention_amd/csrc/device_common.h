@@ -71,6 +71,19 @@ template <> __device__ __forceinline__ f32x16 mfma16<F16>(u32x4 a, u32x4 b, f32x
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                    __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
+// 16x16 fp32 block += A(16 x 32) * B(32 x 16), 16-bit inputs, 8 elements per
+// lane and operand: lane l supplies A row (l % 16), contraction slots
+// 8*(l/16) .. +7, and B column (l % 16), the same slots; result register j
+// of lane l is element [4*(l/16) + j][l % 16].
+template <typename Tag> __device__ __forceinline__ f32x4 mfma16x16(u32x4 a, u32x4 b, f32x4 c);
+template <> __device__ __forceinline__ f32x4 mfma16x16<BF16>(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4 mfma16x16<F16>(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
 // fp32 inputs: K = 2, one element per lane and operand.
 __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);

@@ -12,18 +12,29 @@
 // Mapping to gfx950:
 //   * Scores are computed transposed, S^T = K Q^T, on 32x32x16 matrix-core
 //     blocks: a lane owns one query (its column) and half the keys of each
-//     32-key block (its rows), so row max and row sum are in-lane but for one
-//     exchange between the two lane halves (v_permlane32_swap).
+//     32-key block (its rows), so a row max is in-lane but for one exchange
+//     between the two lane halves (v_permlane32_swap).
 //   * The output is kept transposed too, O^T += V^T P^T: probabilities feed
 //     the second product straight from the score registers (rounded and
 //     packed in pairs), and a rescale touches only the lane's own query.
+//   * Row sums on the matrix core: each 16-key block of rounded
+//     probabilities, as it stands for the output product, is also the B
+//     operand of one 16x16x32 product with a fixed 0/1 selector as A. The
+//     selector routes the 16 keys of query q into the result row that lane q
+//     (and lane q + 32) holds in its first register, so every lane keeps the
+//     whole-row sum of its own query. This replaces 8 pairwise adds per block
+//     on the vector unit, which sets the pace of this loop, by one product
+//     an eighth the size of the output products.
 //   * Software pipeline inside each wave: while the vector unit computes the
 //     softmax of key tile t, the same wave issues the matrix products of
 //     P(t-1) V(t-1) and K(t+1) Q^T, one product between every few
 //     probabilities. On gfx950 a wave's own vector instructions issue while
-//     its matrix product runs. Two wave groups in opposite, barrier-separated
-//     phases (one multiplying while the other computes probabilities) were
-//     measured much slower, so the overlap is arranged within the wave.
+//     its matrix product runs. The probabilities themselves go in three
+//     stages over consecutive product slots (scale and shift, exponential,
+//     rounding), so no vector instruction waits on the one just before it.
+//     Two wave groups in opposite, barrier-separated phases (one multiplying
+//     while the other computes probabilities) were measured much slower, so
+//     the overlap is arranged within the wave.
 //   * K and V tiles travel global -> LDS by direct DMA loads
 //     (global_load_lds_dwordx4) into an NST-stage ring, NST-2 tiles ahead of
 //     the tile whose keys are multiplied (NST-3 for rings of 6 or more
@@ -54,11 +65,10 @@ namespace attn {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
-// The reference max stays while every lane's running sum is at most 2^32
+// The reference max stays while every row's running sum is at most 2^32
 // (bit pattern below). The reference starts at the row's maximum over its
 // first tile, so each row's sum is at least 1 from then on and nothing of
-// weight underflows; a lane whose own keys all sit far below the maximum may
-// hold a tiny or zero sum, which is harmless.
+// weight underflows.
 constexpr uint32_t kSumHiBits = 0x4F800000u;  // 2^32
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -135,7 +145,7 @@ __device__ __forceinline__ void barrier_nofence() {
     asm volatile("" ::: "memory");
 }
 
-// True where a running sum (never negative) passed 2^32, is infinite (a
+// True where a running row sum (never negative) passed 2^32, is infinite (a
 // 16-bit probability overflowed) or is not a number.
 __device__ __forceinline__ bool sum_out_of_range(float l) {
     return __float_as_uint(l) > kSumHiBits;
@@ -347,14 +357,34 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
 
     // ---- running state -----------------------------------------------------
     // m_run: the reference max (log2 units, always finite); l_run: the sum of
-    // this lane's probabilities against it.
+    // the row's probabilities against it, the same in both lane halves. It is
+    // register 0 of lacc, the accumulator of the row-sum products (registers
+    // 1-3 are rows the selector leaves empty and stay 0).
     f32x16 oacc[NQ][D / 32];
+    f32x4 lacc[NQ];
     float m_run[NQ], l_run[NQ], l_old[NQ];
+    // Selector operand (A of the 16x16x32 row-sum product). Lane l holds A
+    // row l % 16 over contraction slots 8*(l/16) .. +7; as B, a probability
+    // block gives slot 8g + i of column c the probability of query c + 16*(g
+    // odd) and key 8*(g >= 2) + i (g = l/16 of the supplying lane). Result
+    // row 4g' of column c sits in register 0 of lane 16g' + c, whose query is
+    // c + 16*(g' odd); that row must gather the slots of the groups g with
+    // the same parity. So A row r is 1 on the slots of group g exactly when r
+    // is 0 or 8 and g is even, or r is 4 or 12 and g is odd.
+    u32x4 sel_ones;
+    {
+        const int r16 = lane & 15, g16 = lane >> 4;
+        const bool on = (g16 & 1) ? (r16 == 4 || r16 == 12) : (r16 == 0 || r16 == 8);
+        const uint32_t one2 = std::is_same<Tag, BF16>::value ? 0x3F803F80u : 0x3C003C00u;
+        const uint32_t w1 = on ? one2 : 0u;
+        sel_ones = u32x4{w1, w1, w1, w1};
+    }
 #pragma unroll
     for (int gq = 0; gq < NQ; ++gq) {
         m_run[gq] = 0.f;
         l_run[gq] = 0.f;
         l_old[gq] = 0.f;
+        lacc[gq] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -377,15 +407,19 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
         oacc[gq][db] = mfma16<Tag>(vop[i / NQ], Pm[gq][kb][u], oacc[gq][db]);
     };
     // Probability pair j of the lane: block (kb, gq) = ((j/8) % KBW, j / (8 KBW)),
-    // result registers r, r+1 with r = 2 (j % 8).
-    auto prob_pair = [&](int j, const SAcc& S, PAcc& Pm, float m, float& l) __attribute__((always_inline)) {
+    // result registers r, r+1 with r = 2 (j % 8); 16-key block u = r / 8.
+    auto prob_pair = [&](int j, const SAcc& S, PAcc& Pm, float m) __attribute__((always_inline)) {
         const int gq = j / (8 * KBW), kb = (j / 8) % KBW, r = 2 * (j % 8);
         // masked scores are -inf and c > 0, so their probabilities are 0
         const float p0 = fast_exp2(fmaf(S[kb][gq][r], c, -m));
         const float p1 = fast_exp2(fmaf(S[kb][gq][r + 1], c, -m));
-        const uint32_t w2 = pack2<Tag>(p0, p1);
-        Pm[gq][kb][r / 8][(r / 2) & 3] = w2;
-        l = dot2_sum<Tag>(w2, l);  // the row sum uses the rounded probabilities
+        Pm[gq][kb][r / 8][(r / 2) & 3] = pack2<Tag>(p0, p1);
+    };
+    // Row sums of 16-key block bj = (gq, kb, u) (pairs 4 bj .. 4 bj + 3) into
+    // lacc: the sums use the rounded probabilities, as the output product does.
+    auto row_sum_block = [&](int bj, const PAcc& Pm) __attribute__((always_inline)) {
+        const int gq = bj / (2 * KBW), kb = (bj / 2) % KBW, u = bj % 2;
+        lacc[gq] = mfma16x16<Tag>(sel_ones, Pm[gq][kb][u], lacc[gq]);
     };
     // Scores of `tile` past the rows' limits (causal, key length) -> -inf.
     auto mask_scores = [&](SAcc& S, int tile) __attribute__((always_inline)) {
@@ -418,19 +452,21 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     };
     // Block gq after a sum left the range: move the reference to the exact
     // running max, rescale l (O by the caller, with the returned factor) and
-    // redo the probabilities. Both lane halves of a query decide alike.
+    // redo the probabilities and their row sums. Both lane halves of a query
+    // hold the same sums and decide alike.
     auto exact_max = [&](int gq, const SAcc& S, PAcc& Pm) __attribute__((always_inline)) -> float {
         const float mxs = row_max(gq, S);
-        const float l_row_old = l_old[gq] + swap_halves(l_old[gq]);
         // nothing accumulated yet: the old reference carries no weight
-        float m_new = l_row_old > 0.f ? fmaxf(m_run[gq], mxs) : mxs;
+        float m_new = l_old[gq] > 0.f ? fmaxf(m_run[gq], mxs) : mxs;
         if (m_new == kNegInf) m_new = m_run[gq];  // every key of the row masked so far
-        const float alpha = l_row_old > 0.f ? fast_exp2(m_run[gq] - m_new) : 1.f;
+        const float alpha = l_old[gq] > 0.f ? fast_exp2(m_run[gq] - m_new) : 1.f;
         m_run[gq] = m_new;
-        float l = l_old[gq] * alpha;
 #pragma unroll
-        for (int j = 0; j < 8 * KBW; ++j) prob_pair(gq * 8 * KBW + j, S, Pm, m_new, l);
-        l_run[gq] = l;
+        for (int j = 0; j < 8 * KBW; ++j) prob_pair(gq * 8 * KBW + j, S, Pm, m_new);
+        lacc[gq] = f32x4{l_old[gq] * alpha, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int bj = gq * 2 * KBW; bj < (gq + 1) * 2 * KBW; ++bj) row_sum_block(bj, Pm);
+        l_run[gq] = lacc[gq][0];
         return alpha;
     };
     // After the probabilities of a tile (and the products of the previous
@@ -461,7 +497,8 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     // tiles t+1, t+2 and into the stages of t-3, t-2 --, read K(t+1); mask tile t's scores
     // where some row cannot see all its keys; then the products P(t-1) V(t-1)
     // and K(t+1) Q^T, one at a time, each followed by its share of tile t's
-    // probabilities; check the sums; read V(t) for the next iteration.
+    // probability stages and row-sum products; check the sums; read V(t) for
+    // the next iteration.
     // At t = 0 the output product multiplies zero probabilities; at the last
     // tile the score product reads a stale stage and its result is unused.
     auto iteration = [&](auto par, int t) __attribute__((always_inline)) {
@@ -488,12 +525,47 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
         const unsigned char* kt = stage(t + 1);
         const unsigned char* vt = stage(t > 0 ? t - 1 : 0);
         if (wkey0(t) + KBW * 32 > wave_lim_min) mask_scores(s_cur, t);
-        float l[NQ];
 #pragma unroll
-        for (int gq = 0; gq < NQ; ++gq) {
-            l_old[gq] = l_run[gq];
-            l[gq] = l_run[gq];
-        }
+        for (int gq = 0; gq < NQ; ++gq) l_old[gq] = l_run[gq];
+        // Slot k owns pairs [k NPAIR / NM, (k+1) NPAIR / NM); slot i runs the
+        // exponentials of slot i's pairs, the scale-and-shift of slot i+1's,
+        // the rounding of slot i-1's and the row sums of the blocks whose
+        // last pair slot i-2 owns.
+        float xs[NPAIR][2], es[NPAIR][2];
+        auto pairs = [](int k) { return k * NPAIR / NM; };
+        auto stage_shift = [&](int k) __attribute__((always_inline)) {
+            if (k < 0 || k >= NM) return;
+#pragma unroll
+            for (int j = pairs(k); j < pairs(k + 1); ++j) {
+                const int gq = j / (8 * KBW), kb = (j / 8) % KBW, r = 2 * (j % 8);
+                // masked scores are -inf and c > 0, so their probabilities are 0
+                xs[j][0] = fmaf(s_cur[kb][gq][r], c, -m_run[gq]);
+                xs[j][1] = fmaf(s_cur[kb][gq][r + 1], c, -m_run[gq]);
+            }
+        };
+        auto stage_exp = [&](int k) __attribute__((always_inline)) {
+            if (k < 0 || k >= NM) return;
+#pragma unroll
+            for (int j = pairs(k); j < pairs(k + 1); ++j) {
+                es[j][0] = fast_exp2(xs[j][0]);
+                es[j][1] = fast_exp2(xs[j][1]);
+            }
+        };
+        auto stage_round = [&](int k) __attribute__((always_inline)) {
+            if (k < 0 || k >= NM) return;
+#pragma unroll
+            for (int j = pairs(k); j < pairs(k + 1); ++j) {
+                const int gq = j / (8 * KBW), kb = (j / 8) % KBW, r = 2 * (j % 8);
+                p_cur[gq][kb][r / 8][(r / 2) & 3] = pack2<Tag>(es[j][0], es[j][1]);
+            }
+        };
+        auto stage_sum = [&](int k) __attribute__((always_inline)) {
+            if (k < 0 || k >= NM) return;
+#pragma unroll
+            for (int j = pairs(k); j < pairs(k + 1); ++j)
+                if (j % 4 == 3) row_sum_block(j / 4, p_cur);
+        };
+        stage_shift(0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
@@ -503,15 +575,17 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
             if (f >= NPV && f < NM && (f - NPV) % NQ == 0) read_kop((f - NPV) / NQ, kt);
             if (i < LA && i >= NPV && (i - NPV) % NQ == 0) read_kop((i - NPV) / NQ, kt);
             if (i < NPV) pv_mfma(i, p_prv); else qk_mfma(i - NPV, s_nxt);
-#pragma unroll
-            for (int j = i * NPAIR / NM; j < (i + 1) * NPAIR / NM; ++j) {
-                const int gq = j / (8 * KBW);
-                prob_pair(j, s_cur, p_cur, m_run[gq], l[gq]);
-            }
+            stage_exp(i);
+            stage_shift(i + 1);
+            stage_round(i - 1);
+            stage_sum(i - 2);
             __builtin_amdgcn_sched_barrier(0);
         }
+        stage_round(NM - 1);
+        stage_sum(NM - 2);
+        stage_sum(NM - 1);
 #pragma unroll
-        for (int gq = 0; gq < NQ; ++gq) l_run[gq] = l[gq];
+        for (int gq = 0; gq < NQ; ++gq) l_run[gq] = lacc[gq][0];
         fix_range(s_cur, p_cur);
         read_v_carry(t);
     };
@@ -600,12 +674,11 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
             for (int gq = 0; gq < NQ; ++gq) {
                 const float mb = mrg[(NQ * (D / 32) * 16 + 2 * gq) * 64 + lane];
                 const float lb = mrg[(NQ * (D / 32) * 16 + 2 * gq + 1) * 64 + lane];
-                // both lane halves of a query decide alike: use the row sums
-                const float la_row = l_run[gq] + swap_halves(l_run[gq]);
-                const float lb_row = lb + swap_halves(lb);
-                const float mm = la_row == 0.f ? mb : (lb_row == 0.f ? m_run[gq] : fmaxf(m_run[gq], mb));
-                const float wa = la_row == 0.f ? 0.f : fast_exp2(m_run[gq] - mm);
-                const float wb = lb_row == 0.f ? 0.f : fast_exp2(mb - mm);
+                // l holds whole-row sums: both lane halves of a query decide alike
+                const float la = l_run[gq];
+                const float mm = la == 0.f ? mb : (lb == 0.f ? m_run[gq] : fmaxf(m_run[gq], mb));
+                const float wa = la == 0.f ? 0.f : fast_exp2(m_run[gq] - mm);
+                const float wb = lb == 0.f ? 0.f : fast_exp2(mb - mm);
                 m_run[gq] = mm;
                 l_run[gq] = l_run[gq] * wa + lb * wb;
 #pragma unroll
@@ -627,7 +700,7 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
             for (int gq = 0; gq < NQ; ++gq) {
                 const int qi = qw0 + gq * 32 + n32;
                 if (qi >= p.Sq) continue;
-                const float lt = l_run[gq] + swap_halves(l_run[gq]);
+                const float lt = l_run[gq];
                 float* rec = p.ws + ((((int64_t)b * p.H + h) * p.Sq + qi) * p.n_split + split) * (D + 4);
                 if (hh == 0) {
                     rec[0] = lt > 0.f ? m_run[gq] : kNegInf;
@@ -651,7 +724,7 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
         T* Os = reinterpret_cast<T*>(smem) + wq * 32 * NQ * OROW;
 #pragma unroll
         for (int gq = 0; gq < NQ; ++gq) {
-            const float lt = l_run[gq] + swap_halves(l_run[gq]);
+            const float lt = l_run[gq];
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
             const int qi = qw0 + gq * 32 + n32;
             if (hh == 0 && p.lse != nullptr && qi < p.Sq)
@@ -731,9 +804,11 @@ hipError_t launch16(const FwdArgs& a, hipStream_t stream) {
 
 // ---- tile variants and their choice ----------------------------------------
 // Tile sizes are not probed at run time: the candidates below are compiled in
-// (each without register spills at its waves per SIMD), and a table made
-// offline by timing every candidate over a grid of shapes (tile_table.inc)
-// names the variant per head size, masking, key length and query rows.
+// (none spills registers inside its key loop at its waves per SIMD; the
+// deepest rings keep a few values that live across the loop in scratch), and
+// a table made offline by timing every candidate over a grid of shapes
+// (tile_table.inc) names the variant per head size, masking, key length and
+// query rows.
 struct Variant16 {
     int nq, bn, nst, ksplit, lds;
     hipError_t (*run[2][2])(const FwdArgs&, hipStream_t);  // [whole keys, key splits][fp16, bf16]
