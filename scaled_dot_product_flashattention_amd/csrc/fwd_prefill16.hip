@@ -39,7 +39,8 @@
 //     (global_load_lds_dwordx4) into an NST-stage ring, NST-2 tiles ahead of
 //     the tile whose keys are multiplied (NST-3 for rings of 6 or more
 //     stages, which pass one barrier per two tiles); no registers are spent
-//     on staging.
+//     on staging. At head size 64 four waves issue them (with two key
+//     halves, the waves of half 0, which run ahead of their SIMD partners).
 //     Both sit in LDS row-major with their 16-byte chunks XOR-swizzled per
 //     row so that the K operand reads (ds_read_b128) and the transposing V
 //     operand reads (ds_read_b64_tr_b16) are free of bank conflicts.
@@ -167,13 +168,20 @@ __device__ __forceinline__ bool sum_out_of_range(float l) {
 //          the ranges of a row combine exactly by the block rule.
 template <typename Tag, int D, int NQ, int BN, int NST, int KSPLIT, int OCC, bool SPLIT>
 __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kernel(Prefill16Params p) {
-    constexpr int NT = 256 * KSPLIT;               // threads
     constexpr int KBW = BN / 32 / KSPLIT;          // 32-key blocks per wave and tile
     constexpr int RB = D * 2;                      // bytes per K/V row
     constexpr int CPR = RB / 16;                   // 16-byte chunks per row
     constexpr int TILE_B = BN * RB;
     constexpr int STAGE_B = 2 * TILE_B;            // K tile, then V tile
-    constexpr int DMA1 = TILE_B / 16 / NT;         // DMA loads per thread, tensor and tile
+    // At head size 64 with two key halves only the four waves of half 0
+    // issue the DMA loads: they win issue arbitration against their SIMD
+    // partners of half 1 and reach each barrier first, so the stall of
+    // issuing (a wave waits while the CU's load queue drains) costs least
+    // there. (At head size 128 the extra offsets of twice the loads per
+    // thread do not fit the registers of the deeper ring.)
+    constexpr int NIW = D == 64 ? 4 : 4 * KSPLIT;  // waves that issue DMA loads
+    constexpr int NIT = NIW * 64;
+    constexpr int DMA1 = TILE_B / 16 / NIT;        // DMA loads per issuing thread, tensor and tile
     constexpr int DPT = 2 * DMA1;                  // ... for K and V
     // Rings of 6 or more stages take one barrier per two tiles (at even t),
     // which costs one stage of lookahead.
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     constexpr int NM = NPV + NQK;
     constexpr int NPAIR = NQ * KBW * 8;            // probability pairs per lane and tile
     static_assert(KBW >= 1 && BN % (32 * KSPLIT) == 0, "key tile must split over the wave groups");
-    static_assert(DMA1 >= 1 && TILE_B % (16 * NT) == 0, "tile must split over the lanes");
+    static_assert(DMA1 >= 1 && TILE_B % (16 * NIT) == 0, "tile must split over the lanes");
     static_assert(P >= 2, "the pipeline needs two tiles in flight");
     static_assert(!BAR2 || P >= 3, "tile t+2 must be issued before the barrier of t");
     static_assert((P - 2) * DPT < 64, "vmcnt range");
@@ -259,20 +267,24 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     u32x4 qop[NQ][D / 16];
 
     // ---- DMA of one K/V tile into LDS stage tile % NST ----------------------
-    // Thread-slot i*NT + tid of the tile is the 16-byte chunk (row, pc); it
-    // holds the logical chunk pc ^ swz(row) of key row `row`. Rows at or past
-    // the valid length reread the last valid row (finite, masked later). The
-    // per-thread offsets do not depend on the tile and are computed once.
-    int64_t koff[DMA1], voff[DMA1];
-#pragma unroll
-    for (int i = 0; i < DMA1; ++i) {
-        const int slot = i * NT + tid;
+    // Issuing-thread slot i*NIT + tid of the tile is the 16-byte chunk (row,
+    // pc); it holds the logical chunk pc ^ swz(row) of key row `row`. Rows at
+    // or past the valid length reread the last valid row (finite, masked
+    // later). Pass i covers key rows [i RPP, (i+1) RPP); the swizzles repeat
+    // every 16 rows, so a thread's offsets differ between passes by whole
+    // rows, and the offsets of pass 0 are computed once.
+    constexpr int RPP = NIT / CPR;
+    static_assert(RPP % 16 == 0, "swizzle period must divide the rows per pass");
+    int64_t koff, voff;
+    {
+        const int slot = tid & (NIT - 1);
         const int row = slot / CPR, pc = slot - row * CPR;
-        koff[i] = row * p.sk.s + (pc ^ swz_k<D>(row)) * 8;
-        voff[i] = row * p.sk.s + (pc ^ swz_v<D>(row)) * 8;
+        koff = row * p.sk.s + (pc ^ swz_k<D>(row)) * 8;
+        voff = row * p.sk.s + (pc ^ swz_v<D>(row)) * 8;
     }
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)smem;
     auto issue_tile = [&](int tile) __attribute__((always_inline)) {
+        if (wave >= NIW) return;
         const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + (tile % NST) * STAGE_B + wave * 1024);
         const int key0 = key_lo + tile * BN;
         if (key0 + BN <= nb) {
@@ -280,17 +292,17 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
             const T* vt = vp + key0 * p.sk.s;
 #pragma unroll
             for (int i = 0; i < DMA1; ++i) {
-                dma16(kt + koff[i], st + i * NT * 16);
-                dma16(vt + voff[i], st + i * NT * 16 + TILE_B);
+                dma16(kt + koff + (int64_t)i * RPP * p.sk.s, st + i * NIT * 16);
+                dma16(vt + voff + (int64_t)i * RPP * p.sk.s, st + i * NIT * 16 + TILE_B);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < DMA1; ++i) {
-                const int slot = i * NT + tid;
+                const int slot = i * NIT + tid;
                 const int row = slot / CPR, pc = slot - row * CPR;
                 const int64_t key = min(key0 + row, nb - 1);
-                dma16(kp + key * p.sk.s + (pc ^ swz_k<D>(row)) * 8, st + i * NT * 16);
-                dma16(vp + key * p.sk.s + (pc ^ swz_v<D>(row)) * 8, st + i * NT * 16 + TILE_B);
+                dma16(kp + key * p.sk.s + (pc ^ swz_k<D>(row)) * 8, st + i * NIT * 16);
+                dma16(vp + key * p.sk.s + (pc ^ swz_v<D>(row)) * 8, st + i * NIT * 16 + TILE_B);
             }
         }
     };
@@ -804,8 +816,9 @@ hipError_t launch16(const FwdArgs& a, hipStream_t stream) {
 
 // ---- tile variants and their choice ----------------------------------------
 // Tile sizes are not probed at run time: the candidates below are compiled in
-// (none spills registers inside its key loop at its waves per SIMD; the
-// deepest rings keep a few values that live across the loop in scratch), and
+// (none spills registers in the products of its key loop at its waves per
+// SIMD; the deepest rings keep a few values that live across the loop, or a
+// base address reloaded once per tile, in scratch), and
 // a table made offline by timing every candidate over a grid of shapes
 // (tile_table.inc) names the variant per head size, masking, key length and
 // query rows.
