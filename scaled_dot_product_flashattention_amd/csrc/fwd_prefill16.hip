@@ -242,8 +242,27 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     const int b = bh / p.H;
     const int h = bh - b * p.H;
 
-    const int nb = clamp_len(p.kv_len, b, p.Sk);
     const int q0 = qt * BM;
+    const T* qp = static_cast<const T*>(p.q) + p.sq.head(b, h);
+    const int qw0 = q0 + wq * 32 * NQ;  // first query row of this wave
+    // ---- Q operands (B of S^T = K Q^T), in registers for the whole loop ----
+    // K-step s holds q[row][16s + 8h .. +7]. Their loads go out first:
+    // nothing in them waits for the per-batch key length, a load of its own
+    // (the fence keeps the compiler from waiting for it earlier).
+    u32x4 qop[NQ][D / 16];
+#pragma unroll
+    for (int gq = 0; gq < NQ; ++gq) {
+        const int qi = qw0 + gq * 32 + n32;
+        const bool ok = qi < p.Sq;
+        const T* row = qp + (int64_t)(ok ? qi : 0) * p.sq.s;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            qop[gq][s] = ok ? *reinterpret_cast<const u32x4*>(row + s * 16 + hh * 8) : z;
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int nb = clamp_len(p.kv_len, b, p.Sk);
     const int q_end = min(q0 + BM, p.Sq);
     const int kend = p.causal ? min(nb, q_end) : nb;  // keys any row of the tile can see
     const int key_lo = SPLIT ? split * p.chunk : 0;   // this workgroup's keys: [key_lo, key_hi)
@@ -251,20 +270,14 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     const int ntiles = key_hi > key_lo ? (key_hi - key_lo + BN - 1) / BN : 0;
     const int lim_hi = SPLIT ? key_hi : nb;  // keys from here on are masked for every row
 
-    const T* qp = static_cast<const T*>(p.q) + p.sq.head(b, h);
     const T* kp = static_cast<const T*>(p.k) + p.sk.head(b, h);
     const T* vp = static_cast<const T*>(p.v) + p.sk.head(b, h);
     T* op = static_cast<T*>(p.o) + p.sq.head(b, h);
 
-    const int qw0 = q0 + wq * 32 * NQ;  // first query row of this wave
     // Waves past the last query row compute on zero queries and store nothing.
     const int wave_lim_min = p.causal ? min(lim_hi, qw0 + 1) : lim_hi;  // keys past this need masks
     // first key of this wave's part of `tile`
     auto wkey0 = [&](int tile) __attribute__((always_inline)) { return key_lo + tile * BN + kb0 * 32; };
-
-    // Q operands (B of S^T = K Q^T), in registers for the whole loop: K-step
-    // s holds q[row][16s + 8h .. +7]. Loaded with the first DMA tile below.
-    u32x4 qop[NQ][D / 16];
 
     // ---- DMA of one K/V tile into LDS stage tile % NST ----------------------
     // Issuing-thread slot i*NIT + tid of the tile is the 16-byte chunk (row,
@@ -602,21 +615,10 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
         read_v_carry(t);
     };
 
-    // Tile 0 and the Q operands load together (one wait covers both); the
-    // rest of the ring goes out after it.
+    // The Q operands and tile 0 load together (one wait covers both); the
+    // Q loads go first, as they do not wait for the key length. The rest of
+    // the ring goes out after the wait.
     if (ntiles > 0) issue_tile(0);
-    // ---- Q operands (B of S^T = K Q^T), in registers for the whole loop ----
-#pragma unroll
-    for (int gq = 0; gq < NQ; ++gq) {
-        const int qi = qw0 + gq * 32 + n32;
-        const bool ok = qi < p.Sq;
-        const T* row = qp + (int64_t)(ok ? qi : 0) * p.sq.s;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            qop[gq][s] = ok ? *reinterpret_cast<const u32x4*>(row + s * 16 + hh * 8) : z;
-        }
-    }
     wait_vmcnt<0>();
     for (int t = 1; t < min(P, ntiles); ++t) issue_tile(t);
     if (ntiles > 0) {
