@@ -109,7 +109,7 @@ struct Prefill16Params {
 constexpr int lds_bytes16(int D, int NQ, int BN, int NST, int KSPLIT) {
     const int ring = NST * 2 * BN * D * 2;
     const int out = 4 * 32 * NQ * (D + 8) * 2;
-    const int mrg = KSPLIT == 2 ? 4 * (NQ * (D / 32) * 16 + 2 * NQ) * 64 * 4 : 0;
+    const int mrg = KSPLIT == 2 ? 8 * (NQ * (D / 64) * 16 + 2 * NQ) * 64 * 4 : 0;
     const int a = ring > out ? ring : out;
     return a > mrg ? a : mrg;
 }
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     constexpr bool BAR2 = NST >= 6;
     constexpr int P = BAR2 ? NST - 3 : NST - 2;    // tiles issued ahead
     constexpr int OROW = D + 8;                    // output staging row (elements)
-    constexpr int MRG_W = (NQ * (D / 32) * 16 + 2 * NQ) * 64 * 4;  // one wave's (O, m, l) in fp32
+    constexpr int MRG_W = (NQ * (D / 64) * 16 + 2 * NQ) * 64 * 4;  // half a wave's O, its (m, l), fp32
     constexpr int LDS_B = lds_bytes16(D, NQ, BN, NST, KSPLIT);
     constexpr int NPV = KBW * 2 * (D / 32) * NQ;   // products of P V per tile and wave
     constexpr int NQK = (D / 16) * KBW * NQ;       // products of K Q^T per tile and wave
@@ -668,104 +668,125 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     // ---- merge the two key halves (KSPLIT = 2) ------------------------------
     // Lane (n32, h) of waves w and w+4 holds the same queries and the same
     // rows of O^T over disjoint keys: O = O_a 2^(m_a - m) + O_b 2^(m_b - m),
-    // where a half with nothing accumulated (l = 0) has no weight.
-    if constexpr (KSPLIT == 2) {
-        float* mrg = reinterpret_cast<float*>(smem) + wq * (MRG_W / 4);
-        if (kh == 1) {
+    // where a half with nothing accumulated (l = 0) has no weight. Each half
+    // finishes half of the head dimension: half kh keeps the 32-column blocks
+    // [kh DB/2, (kh+1) DB/2) and hands the others, with its (m, l), to its
+    // partner through LDS. Both halves then compute the same (m, l).
+    constexpr int DB = D / 32;
+    constexpr int DBH = KSPLIT == 2 ? DB / 2 : DB;  // blocks finished by each wave
+    // The rest runs with the wave's key half as a constant, so that the
+    // accumulator blocks it finishes are indexed at compile time.
+    auto finish = [&](auto khc) __attribute__((always_inline)) {
+        constexpr int KH = decltype(khc)::value;
+        constexpr int db0 = KSPLIT == 2 ? KH * DBH : 0;  // first block this wave finishes
+        if constexpr (KSPLIT == 2) {
+            float* mine = reinterpret_cast<float*>(smem) + (KH * 4 + wq) * (MRG_W / 4);
+            const float* theirs = reinterpret_cast<const float*>(smem) + ((KH ^ 1) * 4 + wq) * (MRG_W / 4);
 #pragma unroll
             for (int gq = 0; gq < NQ; ++gq) {
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db)
+                for (int j = 0; j < DBH; ++j) {
+                    const int db = (KH ^ 1) * DBH + j;  // the partner's blocks
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) mrg[((gq * (D / 32) + db) * 16 + r) * 64 + lane] = oacc[gq][db][r];
-                mrg[(NQ * (D / 32) * 16 + 2 * gq) * 64 + lane] = m_run[gq];
-                mrg[(NQ * (D / 32) * 16 + 2 * gq + 1) * 64 + lane] = l_run[gq];
+                    for (int r = 0; r < 16; ++r) mine[((gq * DBH + j) * 16 + r) * 64 + lane] = oacc[gq][db][r];
+                }
+                mine[(NQ * DBH * 16 + 2 * gq) * 64 + lane] = m_run[gq];
+                mine[(NQ * DBH * 16 + 2 * gq + 1) * 64 + lane] = l_run[gq];
             }
-        }
-        __syncthreads();
-        if (kh == 0) {
+            __syncthreads();
 #pragma unroll
             for (int gq = 0; gq < NQ; ++gq) {
-                const float mb = mrg[(NQ * (D / 32) * 16 + 2 * gq) * 64 + lane];
-                const float lb = mrg[(NQ * (D / 32) * 16 + 2 * gq + 1) * 64 + lane];
+                const float mb = theirs[(NQ * DBH * 16 + 2 * gq) * 64 + lane];
+                const float lb = theirs[(NQ * DBH * 16 + 2 * gq + 1) * 64 + lane];
                 // l holds whole-row sums: both lane halves of a query decide alike
                 const float la = l_run[gq];
-                const float mm = la == 0.f ? mb : (lb == 0.f ? m_run[gq] : fmaxf(m_run[gq], mb));
-                const float wa = la == 0.f ? 0.f : fast_exp2(m_run[gq] - mm);
+                const float ma = m_run[gq];
+                const float mm = la == 0.f ? mb : (lb == 0.f ? ma : fmaxf(ma, mb));
+                const float wa = la == 0.f ? 0.f : fast_exp2(ma - mm);
                 const float wb = lb == 0.f ? 0.f : fast_exp2(mb - mm);
+                // the same expression in both halves (KH 0 holds "a"): identical bits
+                const float l0 = KH == 0 ? la : lb, w0 = KH == 0 ? wa : wb;
+                const float l1 = KH == 0 ? lb : la, w1 = KH == 0 ? wb : wa;
                 m_run[gq] = mm;
-                l_run[gq] = l_run[gq] * wa + lb * wb;
+                l_run[gq] = l0 * w0 + l1 * w1;
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db)
+                for (int j = 0; j < DBH; ++j)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        oacc[gq][db][r] = oacc[gq][db][r] * wa + mrg[((gq * (D / 32) + db) * 16 + r) * 64 + lane] * wb;
+                        oacc[gq][db0 + j][r] = oacc[gq][db0 + j][r] * wa + theirs[((gq * DBH + j) * 16 + r) * 64 + lane] * wb;
             }
+            __syncthreads();
         }
-        __syncthreads();
-    }
 
-    // ---- epilogue of a key range: the rows' records --------------------------
-    // Lane (n32, h) holds o[d] for d = db*32 + 8jj + 4h + e, e = 0..3: one
-    // 16-byte store each.
-    if constexpr (SPLIT) {
-        if (kh == 0) {
+        // ---- epilogue of a key range: the rows' records --------------------------
+        // Lane (n32, h) holds o[d] for d = db*32 + 8jj + 4h + e, e = 0..3: one
+        // 16-byte store each.
+        if constexpr (SPLIT) {
 #pragma unroll
             for (int gq = 0; gq < NQ; ++gq) {
                 const int qi = qw0 + gq * 32 + n32;
                 if (qi >= p.Sq) continue;
                 const float lt = l_run[gq];
                 float* rec = p.ws + ((((int64_t)b * p.H + h) * p.Sq + qi) * p.n_split + split) * (D + 4);
-                if (hh == 0) {
+                if (hh == 0 && KH == 0) {
                     rec[0] = lt > 0.f ? m_run[gq] : kNegInf;
                     rec[1] = lt;
                 }
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db)
+                for (int j = 0; j < DBH; ++j)
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
+                        const int db = db0 + j;
                         const f32x16& ov = oacc[gq][db];
                         *reinterpret_cast<f32x4*>(rec + 4 + db * 32 + 8 * jj + 4 * hh) =
                             f32x4{ov[4 * jj], ov[4 * jj + 1], ov[4 * jj + 2], ov[4 * jj + 3]};
                     }
             }
+            return;
         }
-        return;
-    }
 
-    // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2 -------------------
-    if (kh == 0) {
-        T* Os = reinterpret_cast<T*>(smem) + wq * 32 * NQ * OROW;
+        // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2 -------------------
+        // Each wave stages its blocks of the head dimension; the rows of a query
+        // group are then stored by both of its waves, half each.
+        {
+            T* Os = reinterpret_cast<T*>(smem) + wq * 32 * NQ * OROW;
 #pragma unroll
-        for (int gq = 0; gq < NQ; ++gq) {
-            const float lt = l_run[gq];
-            const float inv = lt > 0.f ? 1.f / lt : 0.f;
-            const int qi = qw0 + gq * 32 + n32;
-            if (hh == 0 && p.lse != nullptr && qi < p.Sq)
-                p.lse[((int64_t)b * p.H + h) * p.Sq + qi] = lt > 0.f ? (m_run[gq] + log2f(lt)) * kLn2 : kNegInf;
-            T* orow = Os + (gq * 32 + n32) * OROW;
+            for (int gq = 0; gq < NQ; ++gq) {
+                const float lt = l_run[gq];
+                const float inv = lt > 0.f ? 1.f / lt : 0.f;
+                const int qi = qw0 + gq * 32 + n32;
+                if (hh == 0 && KH == 0 && p.lse != nullptr && qi < p.Sq)
+                    p.lse[((int64_t)b * p.H + h) * p.Sq + qi] = lt > 0.f ? (m_run[gq] + log2f(lt)) * kLn2 : kNegInf;
+                T* orow = Os + (gq * 32 + n32) * OROW;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
+                for (int j = 0; j < DBH; ++j)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int d0 = db * 32 + 8 * jj + 4 * hh;
-                    const f32x16& ov = oacc[gq][db];
-                    const u32x2 pk2 = {pack2<Tag>(ov[4 * jj] * inv, ov[4 * jj + 1] * inv),
-                                       pack2<Tag>(ov[4 * jj + 2] * inv, ov[4 * jj + 3] * inv)};
-                    *reinterpret_cast<u32x2*>(orow + d0) = pk2;
-                }
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int db = db0 + j;
+                        const int d0 = db * 32 + 8 * jj + 4 * hh;
+                        const f32x16& ov = oacc[gq][db];
+                        const u32x2 pk2 = {pack2<Tag>(ov[4 * jj] * inv, ov[4 * jj + 1] * inv),
+                                           pack2<Tag>(ov[4 * jj + 2] * inv, ov[4 * jj + 3] * inv)};
+                        *reinterpret_cast<u32x2*>(orow + d0) = pk2;
+                    }
+            }
         }
-    }
-    __syncthreads();
-    if (kh == 0) {
-        const T* Os = reinterpret_cast<const T*>(smem) + wq * 32 * NQ * OROW;
-        for (int cidx = lane; cidx < 32 * NQ * CPR; cidx += 64) {
-            const int row = cidx / CPR, cc = cidx - row * CPR;
-            const int qi = qw0 + row;
-            if (qi < p.Sq)
-                *reinterpret_cast<u32x4*>(op + (int64_t)qi * p.sq.s + cc * 8) =
-                    *reinterpret_cast<const u32x4*>(Os + row * OROW + cc * 8);
+        __syncthreads();
+        {
+            const T* Os = reinterpret_cast<const T*>(smem) + wq * 32 * NQ * OROW;
+            for (int cidx = KH * 64 + lane; cidx < 32 * NQ * CPR; cidx += 64 * KSPLIT) {
+                const int row = cidx / CPR, cc = cidx - row * CPR;
+                const int qi = qw0 + row;
+                if (qi < p.Sq)
+                    *reinterpret_cast<u32x4*>(op + (int64_t)qi * p.sq.s + cc * 8) =
+                        *reinterpret_cast<const u32x4*>(Os + row * OROW + cc * 8);
+            }
         }
+    };
+    if constexpr (KSPLIT == 1) {
+        finish(int_c<0>{});
+    } else {
+        if (kh == 0) finish(int_c<0>{}); else finish(int_c<1>{});
     }
 }
 
