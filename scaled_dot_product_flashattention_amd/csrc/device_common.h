@@ -92,17 +92,6 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
 // Base-2 exponential on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Sum of a packed pair of 16-bit values, accumulated in fp32 (v_dot2 with 1, 1).
-template <typename Tag> __device__ __forceinline__ float dot2_sum(uint32_t w, float acc);
-template <> __device__ __forceinline__ float dot2_sum<BF16>(uint32_t w, float acc) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
-}
-template <> __device__ __forceinline__ float dot2_sum<F16>(uint32_t w, float acc) {
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
-}
-
 // Value of the lane in the other half of the wave (lane ^ 32).
 __device__ __forceinline__ float swap_halves(float x) {
     const uint32_t u = __float_as_uint(x);

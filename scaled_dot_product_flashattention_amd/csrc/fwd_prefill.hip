@@ -1,4 +1,5 @@
-// Fused attention forward: one kernel, scores and probabilities stay on chip.
+// Fused attention forward for fp32 inputs: one kernel, scores and
+// probabilities stay on chip (16-bit inputs run fwd_prefill16.hip).
 //
 // Method (chapter "2. 自注意力机制算子…以及FlashAttention优化", §2.6, and the
 // section "FlashAttention 分块计算原理与浏览器适配" of the WebGPU page): the
@@ -11,8 +12,8 @@
 //
 // Mapping to gfx950:
 //   * 4 waves per workgroup, each owning 32*NQ query rows; BM = 128*NQ.
-//   * Scores are computed transposed, S^T = K Q^T, with 32x32 matrix-core
-//     blocks: a lane then owns one query (its column) and 32 of the 64 keys
+//   * Scores are computed transposed, S^T = K Q^T, with 32x32x2 fp32
+//     matrix-core blocks: a lane then owns one query (its column) and 32 of the 64 keys
 //     of a tile (its rows), so the row max and row sum are in-lane except for
 //     one exchange between the two lane halves.
 //   * The output is kept transposed too, O^T += V^T P^T: the probabilities
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(PrefillParams p) {
     using C = PrefillCfg<Tag, D, NQ>;
     using T = typename Tag::storage;
     constexpr int BN = C::BN;
-    constexpr bool k16 = (C::ES == 2);
+    static_assert(C::ES == 4, "fp32 inputs only");
 
     __shared__ __align__(16) unsigned char smem[C::LDS_BYTES];
 
@@ -115,36 +116,25 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(PrefillParams p) {
     const int wave_lim_min = p.causal ? min(nb, qw0 + 1) : nb;  // tiles past this need masks
 
     // ---- Q operands, held in registers for the whole key loop -------------
-    // 16-bit: B operand of S^T = K Q^T, K-step s holds q[row][16s + 8h .. +7].
-    // fp32:   K-step s holds q[row][2s + h].
-    constexpr int QSTEPS = k16 ? D / 16 : D / 2;
-    typedef typename std::conditional<k16, u32x4, float>::type QOp;
-    QOp qop[NQ][QSTEPS];
+    // B operand of S^T = K Q^T: K-step s holds q[row][2s + h].
+    constexpr int QSTEPS = D / 2;
+    float qop[NQ][QSTEPS];
 #pragma unroll
     for (int gq = 0; gq < NQ; ++gq) {
         const int qi = qw0 + gq * 32 + n32;
         const bool ok = qi < p.Sq;
         const T* row = qp + (int64_t)(ok ? qi : 0) * p.sq.s;
 #pragma unroll
-        for (int s = 0; s < QSTEPS; ++s) {
-            if constexpr (k16) {
-                u32x4 z = {0u, 0u, 0u, 0u};
-                qop[gq][s] = ok ? *reinterpret_cast<const u32x4*>(row + s * 16 + hh * 8) : z;
-            } else {
-                qop[gq][s] = ok ? row[2 * s + hh] : 0.f;
-            }
-        }
+        for (int s = 0; s < QSTEPS; ++s) qop[gq][s] = ok ? row[2 * s + hh] : 0.f;
     }
 
     // ---- global -> register -> LDS staging of one K/V tile -----------------
-    // K: 16-byte chunks, consecutive threads along a row (coalesced).
-    // V (16-bit): pairs of key rows, so the transposed LDS store writes two
-    //   keys (one 32-bit word) per d; V (fp32): single elements.
-    constexpr int VCH = k16 ? (BN / 2) * C::CPR / 256 : BN * C::CPR / 256;
-    constexpr int VREGS = k16 ? 2 : 1;
+    // K and V: 16-byte chunks, consecutive threads along a row (coalesced);
+    // V is transposed element by element when stored to LDS.
+    constexpr int VCH = BN * C::CPR / 256;
     static_assert(VCH >= 1, "V tile must cover all threads");
     u32x4 kreg[C::KCH];
-    u32x4 vreg[VCH][VREGS];
+    u32x4 vreg[VCH];
 
     auto load_k = [&](int t) {
         const int key0 = t * BN;
@@ -163,12 +153,9 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int c = 0; c < VCH; ++c) {
             const int idx = tid + c * 256;
-            const int pr = idx / C::CPR, cc = idx - pr * C::CPR;
-#pragma unroll
-            for (int e = 0; e < VREGS; ++e) {
-                const int key = key0 + pr * VREGS + e;
-                vreg[c][e] = key < nb ? *reinterpret_cast<const u32x4*>(vp + (int64_t)key * p.sk.s + cc * C::EPC) : z;
-            }
+            const int row = idx / C::CPR, cc = idx - row * C::CPR;
+            const int key = key0 + row;
+            vreg[c] = key < nb ? *reinterpret_cast<const u32x4*>(vp + (int64_t)key * p.sk.s + cc * C::EPC) : z;
         }
     };
 
@@ -204,25 +191,15 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(PrefillParams p) {
         for (int s = 0; s < QSTEPS; ++s) {
 #pragma unroll
             for (int kb = 0; kb < BN / 32; ++kb) {
-                const T* krow = Ks + (kb * 32 + n32) * C::KROW;
-                if constexpr (k16) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(krow + s * 16 + hh * 8);
+                const float a = Ks[(kb * 32 + n32) * C::KROW + 2 * s + hh];
 #pragma unroll
-                    for (int gq = 0; gq < NQ; ++gq) sacc[kb][gq] = mfma16<Tag>(a, qop[gq][s], sacc[kb][gq]);
-                } else {
-                    const float a = krow[2 * s + hh];
-#pragma unroll
-                    for (int gq = 0; gq < NQ; ++gq) sacc[kb][gq] = mfma_f32(a, qop[gq][s], sacc[kb][gq]);
-                }
+                for (int gq = 0; gq < NQ; ++gq) sacc[kb][gq] = mfma_f32(a, qop[gq][s], sacc[kb][gq]);
             }
         }
     };
 
     // -- online softmax of one tile: running max (moved lazily), probabilities
-    //    rounded to the input type and packed in pairs, running sum -----------
-    // pk[gq][kb][w] holds the probabilities of result registers 2w and 2w+1.
-    constexpr int PKW = k16 ? 8 : 1;
-    uint32_t pk[NQ][BN / 32][PKW];
+    //    in place of the scores, running sum ----------------------------------
     auto softmax_tile = [&](auto masked_tag, f32x16 (&sacc)[BN / 32][NQ], int tile) {
         constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
@@ -276,15 +253,9 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(PrefillParams p) {
                         p0 = (x0 == kNegInf) ? 0.f : p0;
                         p1 = (x1 == kNegInf) ? 0.f : p1;
                     }
-                    if constexpr (k16) {
-                        const uint32_t w2 = pack2<Tag>(p0, p1);
-                        pk[gq][kb][r / 2] = w2;
-                        rs[(r / 2) & 3] = dot2_sum<Tag>(w2, rs[(r / 2) & 3]);
-                    } else {
-                        sacc[kb][gq][r] = p0;
-                        sacc[kb][gq][r + 1] = p1;
-                        rs[(r / 2) & 3] += p0 + p1;
-                    }
+                    sacc[kb][gq][r] = p0;
+                    sacc[kb][gq][r + 1] = p1;
+                    rs[(r / 2) & 3] += p0 + p1;
                 }
             l_run[gq] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
         }
@@ -294,32 +265,13 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(PrefillParams p) {
     auto pv_tile = [&](const T* Vt, f32x16 (&sacc)[BN / 32][NQ]) {
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb) {
-            if constexpr (k16) {
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
+            for (int r = 0; r < 16; ++r) {
 #pragma unroll
-                    for (int db = 0; db < D / 32; ++db) {
-                        const T* vrow = Vt + (db * 32 + n32) * C::VROW + kb * 32 + 16 * u + 4 * hh;
-                        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-                        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-                        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+                for (int db = 0; db < D / 32; ++db) {
+                    const float a = Vt[(db * 32 + n32) * C::VROW + kb * 32 + blk_row(r, hh)];
 #pragma unroll
-                        for (int gq = 0; gq < NQ; ++gq) {
-                            const u32x4 b = {pk[gq][kb][4 * u], pk[gq][kb][4 * u + 1], pk[gq][kb][4 * u + 2],
-                                             pk[gq][kb][4 * u + 3]};
-                            oacc[gq][db] = mfma16<Tag>(a, b, oacc[gq][db]);
-                        }
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-#pragma unroll
-                    for (int db = 0; db < D / 32; ++db) {
-                        const float a = Vt[(db * 32 + n32) * C::VROW + kb * 32 + blk_row(r, hh)];
-#pragma unroll
-                        for (int gq = 0; gq < NQ; ++gq) oacc[gq][db] = mfma_f32(a, sacc[kb][gq][r], oacc[gq][db]);
-                    }
+                    for (int gq = 0; gq < NQ; ++gq) oacc[gq][db] = mfma_f32(a, sacc[kb][gq][r], oacc[gq][db]);
                 }
             }
         }
@@ -346,14 +298,10 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int c2 = 0; c2 < VCH; ++c2) {
             const int idx = tid + c2 * 256;
-            const int pr = idx / C::CPR, cc = idx - pr * C::CPR;
-            if constexpr (k16) {
-                store_pair_transposed(Vt, C::VROW, cc, pr, vreg[c2][0], vreg[c2][1]);
-            } else {
+            const int row = idx / C::CPR, cc = idx - row * C::CPR;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    reinterpret_cast<uint32_t*>(Vt)[(cc * 4 + e) * C::VROW + pr] = vreg[c2][0][e];
-            }
+            for (int e = 0; e < 4; ++e)
+                reinterpret_cast<uint32_t*>(Vt)[(cc * 4 + e) * C::VROW + row] = vreg[c2][e];
         }
     };
 
@@ -420,15 +368,9 @@ __global__ __launch_bounds__(256, 2) void fwd_prefill_kernel(PrefillParams p) {
             for (int jj = 0; jj < 4; ++jj) {
                 const int d0 = db * 32 + 8 * jj + 4 * hh;
                 const f32x16& ov = oacc[gq][db];
-                if constexpr (k16) {
-                    const u32x2 pk = {pack2<Tag>(ov[4 * jj] * inv, ov[4 * jj + 1] * inv),
-                                      pack2<Tag>(ov[4 * jj + 2] * inv, ov[4 * jj + 3] * inv)};
-                    *reinterpret_cast<u32x2*>(orow + d0) = pk;
-                } else {
-                    const f32x4 pk = {ov[4 * jj] * inv, ov[4 * jj + 1] * inv, ov[4 * jj + 2] * inv,
-                                      ov[4 * jj + 3] * inv};
-                    *reinterpret_cast<f32x4*>(orow + d0) = pk;
-                }
+                const f32x4 o4 = {ov[4 * jj] * inv, ov[4 * jj + 1] * inv, ov[4 * jj + 2] * inv,
+                                  ov[4 * jj + 3] * inv};
+                *reinterpret_cast<f32x4*>(orow + d0) = o4;
             }
     }
     __syncthreads();
