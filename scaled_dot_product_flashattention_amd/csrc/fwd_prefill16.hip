@@ -177,8 +177,8 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     // issue the DMA loads: they win issue arbitration against their SIMD
     // partners of half 1 and reach each barrier first, so the stall of
     // issuing (a wave waits while the CU's load queue drains) costs least
-    // there. (At head size 128 the extra offsets of twice the loads per
-    // thread do not fit the registers of the deeper ring.)
+    // there. (At head size 128 the 5-stage variant then spilled registers
+    // inside its key loop, so all eight waves issue there.)
     constexpr int NIW = D == 64 ? 4 : 4 * KSPLIT;  // waves that issue DMA loads
     constexpr int NIT = NIW * 64;
     constexpr int DMA1 = TILE_B / 16 / NIT;        // DMA loads per issuing thread, tensor and tile
