@@ -46,7 +46,8 @@
 //     operand reads (ds_read_b64_tr_b16) are free of bank conflicts.
 //   * KSPLIT = 2: two groups of 4 waves take the two key halves of every
 //     tile for the same queries (each key operand then feeds two query
-//     blocks), and merge their (m, l, O) through LDS at the end.
+//     blocks), and merge their (m, l, O) through LDS at the end. Their Q
+//     rows are loaded once, into LDS, and read from there by both groups.
 //   * The running max is a reference: it starts at the exact maximum of
 //     each row over the wave's first key tile, and later probabilities are
 //     taken against it directly; only the row sum is checked. The exact max
@@ -250,15 +251,37 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     // nothing in them waits for the per-batch key length, a load of its own
     // (the fence keeps the compiler from waiting for it earlier).
     u32x4 qop[NQ][D / 16];
+    // With two key halves both waves of a query group need the same Q: the
+    // first four waves load the workgroup's BM rows once, by DMA, into LDS
+    // stages P.. (untouched until the first iteration's barrier), and every
+    // wave reads its operands from there after the prologue's barrier.
+    constexpr bool QLDS = KSPLIT == 2;
+    constexpr int QOFF = P * STAGE_B;  // LDS byte offset of the staged Q rows
+    static_assert(!QLDS || QOFF + BM * RB <= NST * STAGE_B, "staged Q must fit the free stages");
+    if constexpr (QLDS) {
+        if (wave < 4) {
+            const uint32_t st = __builtin_amdgcn_readfirstlane(
+                (uint32_t)(uintptr_t)(lds_void*)smem + QOFF + wave * 1024);
 #pragma unroll
-    for (int gq = 0; gq < NQ; ++gq) {
-        const int qi = qw0 + gq * 32 + n32;
-        const bool ok = qi < p.Sq;
-        const T* row = qp + (int64_t)(ok ? qi : 0) * p.sq.s;
+            for (int i = 0; i < BM * CPR / 256; ++i) {
+                const int slot = i * 256 + tid;
+                const int row = slot / CPR, pc = slot - row * CPR;
+                // rows past the last query reread it (finite; never stored)
+                const int64_t qi = min(q0 + row, p.Sq - 1);
+                dma16(qp + qi * p.sq.s + (pc ^ swz_k<D>(row)) * 8, st + i * 256 * 16);
+            }
+        }
+    } else {
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            qop[gq][s] = ok ? *reinterpret_cast<const u32x4*>(row + s * 16 + hh * 8) : z;
+        for (int gq = 0; gq < NQ; ++gq) {
+            const int qi = qw0 + gq * 32 + n32;
+            const bool ok = qi < p.Sq;
+            const T* row = qp + (int64_t)(ok ? qi : 0) * p.sq.s;
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) {
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                qop[gq][s] = ok ? *reinterpret_cast<const u32x4*>(row + s * 16 + hh * 8) : z;
+            }
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -621,8 +644,19 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     if (ntiles > 0) issue_tile(0);
     wait_vmcnt<0>();
     for (int t = 1; t < min(P, ntiles); ++t) issue_tile(t);
+    if constexpr (QLDS) {
+        barrier_nofence();  // the staged Q rows have landed for every wave
+#pragma unroll
+        for (int gq = 0; gq < NQ; ++gq)
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) {
+                const int row = wq * 32 * NQ + gq * 32 + n32;
+                qop[gq][s] = *reinterpret_cast<const u32x4*>(smem + QOFF + row * RB +
+                                                             (((2 * s + hh) ^ swz_k<D>(row)) << 4));
+            }
+    }
     if (ntiles > 0) {
-        barrier_nofence();
+        if constexpr (!QLDS) barrier_nofence();
 #pragma unroll
         for (int o = 0; o < NK; ++o) read_kop(o, stage(0));
 #pragma unroll
