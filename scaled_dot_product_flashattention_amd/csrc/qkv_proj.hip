@@ -25,10 +25,14 @@
 //     ahead), rows of 128 B with their 16-byte chunks XOR-swizzled so the
 //     ds_read_b128 operand reads are free of bank conflicts. A stage is
 //     40 KiB, so two workgroups (8 waves) share a CU.
+//   * Operands are read one 16-deep step ahead, one read after each
+//     product; the barrier of a tile sits after the first product of its
+//     last step, so the queued product covers it.
 //   * When the grid is a multiple of 8, consecutive tiles (token-row major)
 //     go to one XCD, so its L2 serves their shared X and W reads.
 //   * Epilogue: fp32 accumulators -> storage type (round to nearest even)
-//     -> LDS -> 16-byte stores, each chunk of 8 columns placed by (t, h, c).
+//     -> LDS -> 16-byte non-temporal stores, each chunk of 8 columns placed
+//     by (t, h, c).
 //   * Rows past M and columns past N reread the last valid row (finite) and
 //     are not stored.
 #include "device_common.h"
@@ -149,25 +153,56 @@ __global__ __launch_bounds__(QNT, 2) void qkv_proj_kernel(QkvParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b2][r] = 0.f;
 
+    // Operand o of a K-step: o < QWN is W block wn*QWN + o, else X block
+    // wm*QWM + o - QWN. They are double-buffered in registers: while the
+    // products of K-step s run, the operands of K-step s+1 are read, one
+    // after each product.
+    constexpr int NO = QWN + QWM;  // 5 operands
+    constexpr int NP = QWN * QWM;  // 6 products
+    static_assert(NO < NP, "each operand read follows a product");
+    auto read_op = [&](const unsigned char* st, int s, int o) __attribute__((always_inline)) -> u32x4 {
+        return o < QWN ? operand(st + QXTILE, wn * QWN + o, s) : operand(st, wm * QWM + (o - QWN), s);
+    };
+    u32x4 op[2][NO];
     const int nk = p.K / QBK;
     issue(0);
+    qwait_vmcnt<0>();
+    qbarrier();
+    if (nk > 1) issue(1);
+#pragma unroll
+    for (int o = 0; o < NO; ++o) op[0][o] = read_op(smem, 0, o);
     for (int kt = 0; kt < nk; ++kt) {
-        qwait_vmcnt<0>();   // this thread's part of tile kt is in LDS
-        qbarrier();         // everyone's part; everyone is done with tile kt-1
-        if (kt + 1 < nk) issue(kt + 1);
-        const unsigned char* xt = smem + (kt % QNST) * QSTAGE;
-        const unsigned char* wt = xt + QXTILE;
+        const unsigned char* cur = smem + (kt % QNST) * QSTAGE;
+        const unsigned char* nxt = smem + ((kt + 1) % QNST) * QSTAGE;
+        const bool more = kt + 1 < nk;
 #pragma unroll
         for (int s = 0; s < QBK / 16; ++s) {
-            u32x4 wa[QWN], xb[QWM];
+            const u32x4* use = op[s & 1];
+            u32x4* fill = op[(s & 1) ^ 1];
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < QWN; ++j) wa[j] = operand(wt, wn * QWN + j, s);
-#pragma unroll
-            for (int j = 0; j < QWM; ++j) xb[j] = operand(xt, wm * QWM + j, s);
-#pragma unroll
-            for (int a = 0; a < QWN; ++a)
-#pragma unroll
-                for (int b2 = 0; b2 < QWM; ++b2) acc[a][b2] = mfma16<Tag>(wa[a], xb[b2], acc[a][b2]);
+            for (int j = 0; j < NP; ++j) {
+                const int a = j / QWM, b2 = j % QWM;
+                acc[a][b2] = mfma16<Tag>(use[a], use[QWN + b2], acc[a][b2]);
+                if (s + 1 < QBK / 16) {
+                    if (j < NO) fill[j] = read_op(cur, s + 1, j);
+                } else if (more) {
+                    // Last K-step of tile kt, after its first product (the
+                    // operands of this K-step are already in registers):
+                    // tile kt+1 has landed (this thread's loads) and, after
+                    // the barrier, every wave is done reading tile kt, whose
+                    // stage then takes tile kt+2. The operands of tile
+                    // kt+1's first K-step follow the remaining products.
+                    if (j == 0) {
+                        qwait_vmcnt<0>();
+                        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): own reads of tile kt done
+                        qbarrier();
+                        if (kt + 2 < nk) issue(kt + 2);
+                    }
+                    if (j >= 1 && j - 1 < NO) fill[j - 1] = read_op(nxt, 0, j - 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
     __syncthreads();  // all DMA landed and all operand reads done
@@ -199,8 +234,10 @@ __global__ __launch_bounds__(QNT, 2) void qkv_proj_kernel(QkvParams p) {
         const int h = j / p.d, c = j - h * p.d;
         const int b = m / p.S, s = m - b * p.S;
         const int64_t dst = p.so.head(b, h) + (int64_t)s * p.so.s + c;
-        *reinterpret_cast<u32x4*>(static_cast<T*>(p.out[t]) + dst) =
-            *reinterpret_cast<const u32x4*>(Ys + row * QOROW + cc * 8);
+        // streaming stores: the outputs of all workgroups leave at the end
+        // of the launch at once, which non-temporal stores drain faster
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(Ys + row * QOROW + cc * 8),
+                                    reinterpret_cast<u32x4*>(static_cast<T*>(p.out[t]) + dst));
     }
 }
 
