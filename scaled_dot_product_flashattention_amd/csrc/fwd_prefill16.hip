@@ -788,7 +788,11 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
 
         // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2 -------------------
         // Each wave stages its blocks of the head dimension; the rows of a query
-        // group are then stored by both of its waves, half each.
+        // group are then stored by both of its waves, half each. An 8-byte
+        // write pass covers 16 consecutive rows on 32 banks, where rows OROW
+        // elements apart meet in pairs (r and r + 8): rows with bit 3 set swap
+        // the two 8-byte halves of each 16-byte chunk, and the store loop
+        // swaps them back.
         {
             T* Os = reinterpret_cast<T*>(smem) + wq * 32 * NQ * OROW;
 #pragma unroll
@@ -799,12 +803,13 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
                 if (hh == 0 && KH == 0 && p.lse != nullptr && qi < p.Sq)
                     p.lse[((int64_t)b * p.H + h) * p.Sq + qi] = lt > 0.f ? (m_run[gq] + log2f(lt)) * kLn2 : kNegInf;
                 T* orow = Os + (gq * 32 + n32) * OROW;
+                const int half = hh ^ ((n32 >> 3) & 1);
 #pragma unroll
                 for (int j = 0; j < DBH; ++j)
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const int db = db0 + j;
-                        const int d0 = db * 32 + 8 * jj + 4 * hh;
+                        const int d0 = db * 32 + 8 * jj + 4 * half;
                         const f32x16& ov = oacc[gq][db];
                         const u32x2 pk2 = {pack2<Tag>(ov[4 * jj] * inv, ov[4 * jj + 1] * inv),
                                            pack2<Tag>(ov[4 * jj + 2] * inv, ov[4 * jj + 3] * inv)};
@@ -818,9 +823,11 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
             for (int cidx = KH * 64 + lane; cidx < 32 * NQ * CPR; cidx += 64 * KSPLIT) {
                 const int row = cidx / CPR, cc = cidx - row * CPR;
                 const int qi = qw0 + row;
-                if (qi < p.Sq)
-                    *reinterpret_cast<u32x4*>(op + (int64_t)qi * p.sq.s + cc * 8) =
-                        *reinterpret_cast<const u32x4*>(Os + row * OROW + cc * 8);
+                if (qi < p.Sq) {
+                    u32x4 val = *reinterpret_cast<const u32x4*>(Os + row * OROW + cc * 8);
+                    if ((row >> 3) & 1) val = u32x4{val[2], val[3], val[0], val[1]};
+                    *reinterpret_cast<u32x4*>(op + (int64_t)qi * p.sq.s + cc * 8) = val;
+                }
             }
         }
     };
