@@ -250,6 +250,17 @@ int attn_qkv_proj(const void* x, const void* w, void* q, void* k, void* v, int B
                   int H, int d, int layout, int dtype, void* stream);
 
 /*
+ * Which of the two tilings attn_qkv_proj runs for B*S tokens and 3*H*d
+ * output columns on a GPU with n_cu compute units (attn_qkv_proj uses the
+ * current device's count): 0 = 128 tokens x 192 columns per workgroup, two
+ * workgroups per CU; 1 = 256 x 256, one per CU, taken when it needs clearly
+ * fewer rounds of workgroups over the CUs (large products). Writes it to
+ * *tiling. B, S, H, d, n_cu >= 1 (else ATTN_E_SHAPE); tiling non-NULL (else
+ * ATTN_E_NULLPTR). Host only, for tests and tuning.
+ */
+int attn_qkv_proj_tiling(int B, int S, int H, int d, int n_cu, int* tiling);
+
+/*
  * Row softmax: for each row r of x [rows, n],
  *     y[r, j] = exp(scale*x[r, j] - m_r) / l_r,   lse[r] = m_r + ln l_r,
  * with m_r the row maximum of scale*x and l_r the sum of the shifted

@@ -19,6 +19,7 @@ from .api import (  # noqa: F401
     attn_fwd_workspace_size,
     attn_naive_scratch_size,
     attn_qkv_proj,
+    attn_qkv_proj_tiling,
     attn_softmax_rows,
     attn_splitk_workspace_size,
     attn_status_string,

@@ -91,6 +91,8 @@ def load_library() -> ctypes.CDLL:
     L.attn_fwd_tile_info.restype = i
     L.attn_fwd_tile_choice.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i)]
     L.attn_fwd_tile_choice.restype = i
+    L.attn_qkv_proj_tiling.argtypes = [i, i, i, i, i, ctypes.POINTER(i)]
+    L.attn_qkv_proj_tiling.restype = i
     L.attn_fwd_tiled.argtypes = tensors + [i, i, vp, sz, vp]
     L.attn_fwd_tiled.restype = i
     L.attn_fwd_noalloc.argtypes = tensors + [vp]
@@ -147,6 +149,16 @@ def attn_fwd_tile_choice(B: int, H: int, Sq: int, Sk: int, d: int, dtype: torch.
                                              ctypes.byref(t))
     if rc:
         raise AttnError("attn_fwd_tile_choice", rc)
+    return t.value
+
+
+def attn_qkv_proj_tiling(B: int, S: int, H: int, d: int, n_cu: int) -> int:
+    """Tiling attn_qkv_proj runs for these tokens and columns on n_cu CUs
+    (0: 128 x 192 tiles, 1: 256 x 256)."""
+    t = ctypes.c_int(-1)
+    rc = load_library().attn_qkv_proj_tiling(B, S, H, d, n_cu, ctypes.byref(t))
+    if rc:
+        raise AttnError("attn_qkv_proj_tiling", rc)
     return t.value
 
 

@@ -281,6 +281,14 @@ int attn_qkv_proj(const void* x, const void* w, void* q, void* k, void* v, int B
     return status_of(attn::run_qkv_proj(a, static_cast<hipStream_t>(stream)));
 }
 
+int attn_qkv_proj_tiling(int B, int S, int H, int d, int n_cu, int* tiling) {
+    if (!tiling) return ATTN_E_NULLPTR;
+    if (B < 1 || S < 1 || H < 1 || d < 1 || n_cu < 1) return ATTN_E_SHAPE;
+    if ((int64_t)B * S > INT_MAX || (int64_t)3 * H * d > INT_MAX) return ATTN_E_SHAPE;
+    *tiling = attn::qkv_proj_tiling(B * S, 3 * H * d, n_cu);
+    return ATTN_OK;
+}
+
 int attn_softmax_rows(const void* x, void* y, float* lse, int64_t rows, int n, float scale,
                       int dtype, int mode, void* stream) {
     if (!x || !y) return ATTN_E_NULLPTR;

@@ -66,6 +66,8 @@ struct QkvArgs {
     int dtype;   // 1 = fp16, 2 = bf16
 };
 hipError_t run_qkv_proj(const QkvArgs& a, hipStream_t stream);
+// Tiling of the QKV projection for M tokens and N columns on n_cu CUs (0 or 1).
+int qkv_proj_tiling(int M, int N, int n_cu);
 
 // Row softmax of x [rows, n] (mode 0 online, 1 three-pass).
 struct SoftmaxArgs {

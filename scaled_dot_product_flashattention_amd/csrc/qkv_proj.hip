@@ -14,17 +14,21 @@
 // product are contiguous along the contraction.
 //
 // Mapping to gfx950:
-//   * 192 x 128 output tile per workgroup (192 weight rows = output columns,
-//     128 token rows), 4 waves of 96 x 64 (3 x 2 blocks of 32 x 32). The
-//     products are computed transposed, Y^T = W X^T, on 32x32x16 matrix-core
-//     blocks: A = weight rows, B = token rows. Each K-step of 16 reads 5
-//     operands from LDS for 6 products, which keeps LDS reads below what
-//     the LDS delivers at full matrix-core rate.
-//   * K steps of 64: the 128 x 64 tile of X and the 192 x 64 tile of W go
-//     global -> LDS by direct DMA loads into a two-stage ring (one tile
-//     ahead), rows of 128 B with their 16-byte chunks XOR-swizzled so the
-//     ds_read_b128 operand reads are free of bank conflicts. A stage is
-//     40 KiB, so two workgroups (8 waves) share a CU.
+//   * Two tilings. Tiling 0: 192 x 128 output tile per workgroup (192 weight
+//     rows = output columns, 128 token rows), 4 waves of 96 x 64 (3 x 2
+//     blocks of 32 x 32), two workgroups per CU. Tiling 1: 256 x 256, 8
+//     waves of 128 x 64 (4 x 2 blocks), one workgroup per CU; it loads a
+//     third fewer bytes per product but has half as many workgroups, so it
+//     is taken only when it needs clearly fewer rounds of workgroups over
+//     the CUs than tiling 0 (large products).
+//   * The products are computed transposed, Y^T = W X^T, on 32x32x16
+//     matrix-core blocks: A = weight rows, B = token rows. Each K-step of 16
+//     reads 5 (6) operands from LDS for 6 (8) products, which keeps LDS
+//     reads below what the LDS delivers at full matrix-core rate.
+//   * K steps of 64: the X and W tiles go global -> LDS by direct DMA loads
+//     into a two-stage ring (one tile ahead), rows of 128 B with their
+//     16-byte chunks XOR-swizzled so the ds_read_b128 operand reads are free
+//     of bank conflicts. A stage is 40 KiB (64 KiB).
 //   * Operands are read one 16-deep step ahead, one read after each
 //     product; the barrier of a tile sits after the first product of its
 //     last step, so the queued product covers it.
@@ -42,19 +46,9 @@ namespace attn {
 
 namespace {
 
-constexpr int QBM = 128;  // token rows per workgroup
-constexpr int QBN = 192;  // output columns (weight rows) per workgroup
-constexpr int QBK = 64;   // contraction per stage
-constexpr int QNT = 256;  // threads
-constexpr int QWN = 3;    // 32-column blocks per wave
-constexpr int QWM = 2;    // 32-row blocks per wave
-constexpr int QROW = QBK * 2;               // bytes per LDS row
-constexpr int QXTILE = QBM * QROW;          // bytes of the X tile
-constexpr int QWTILE = QBN * QROW;          // bytes of the W tile
-constexpr int QSTAGE = QXTILE + QWTILE;     // X tile, then W tile
+constexpr int QBK = 64;         // contraction per stage
+constexpr int QROW = QBK * 2;   // bytes per LDS row
 constexpr int QNST = 2;
-constexpr int QOROW = QBN + 8;              // output staging row (elements)
-static_assert(QBM * QOROW * 2 <= QNST * QSTAGE, "output staging fits the ring");
 
 typedef __attribute__((address_space(3))) void lds_void_q;
 
@@ -88,16 +82,39 @@ __device__ __forceinline__ void qbarrier() {
 // XOR swizzle of the 16-byte chunks of a 128-byte LDS row.
 __device__ __forceinline__ int qswz(int row) { return (row >> 1) & 7; }
 
-template <typename Tag>
-__global__ __launch_bounds__(QNT, 2) void qkv_proj_kernel(QkvParams p) {
+// A tiling: BM token rows x BN output columns per workgroup, NW waves on a
+// WGM x (NW / WGM) grid, WPC workgroups per CU.
+template <int BM_, int BN_, int NW_, int WGM_, int WPC_>
+struct QTiling {
+    static constexpr int BM = BM_, BN = BN_, NW = NW_, WGM = WGM_, WPC = WPC_;
+    static constexpr int NT = NW * 64;
+    static constexpr int WGN = NW / WGM;
+    static constexpr int QWM = BM / WGM / 32;   // 32-row blocks per wave
+    static constexpr int QWN = BN / WGN / 32;   // 32-column blocks per wave
+    static constexpr int XTILE = BM * QROW;     // bytes of the X tile
+    static constexpr int WTILE = BN * QROW;     // bytes of the W tile
+    static constexpr int STAGE = XTILE + WTILE; // X tile, then W tile
+    static constexpr int OROW = BN + 8;         // output staging row (elements)
+    static constexpr int RING = QNST * STAGE, OUT = BM * OROW * 2;
+    static constexpr int LDS = RING > OUT ? RING : OUT;
+    static_assert(QWM * WGM * 32 == BM && QWN * WGN * 32 == BN, "waves cover the tile");
+    static_assert(LDS <= 160 * 1024, "LDS of one workgroup");
+};
+using QTiling0 = QTiling<128, 192, 4, 2, 2>;
+using QTiling1 = QTiling<256, 256, 8, 4, 1>;
+
+template <typename Tag, typename C>
+__global__ __launch_bounds__(C::NT, C::WPC) void qkv_proj_kernel(QkvParams p) {
+    constexpr int QNT = C::NT, QWM = C::QWM, QWN = C::QWN, QXTILE = C::XTILE, QWTILE = C::WTILE;
+    constexpr int QSTAGE = C::STAGE, QOROW = C::OROW, QBM = C::BM, QBN = C::BN;
     using T = uint16_t;
-    __shared__ __align__(16) unsigned char smem[QNST * QSTAGE];
+    __shared__ __align__(16) unsigned char smem[C::LDS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1;  // 64-row half of the token rows
-    const int wn = wave & 1;   // 96-column half of the output columns
+    const int wm = wave / C::WGN;  // block of token rows of this wave
+    const int wn = wave % C::WGN;  // block of output columns of this wave
     const int n32 = lane & 31;
     const int hh = lane >> 5;
 
@@ -113,8 +130,8 @@ __global__ __launch_bounds__(QNT, 2) void qkv_proj_kernel(QkvParams p) {
 
     // DMA slots: thread-slot i*QNT + tid of a tile is chunk (row, pc) and
     // holds logical chunk pc ^ swz(row) of that row (rows clamped to valid).
-    constexpr int DMAX = QXTILE / 16 / QNT;  // 4 loads per thread for X
-    constexpr int DMAW = QWTILE / 16 / QNT;  // 6 loads per thread for W
+    constexpr int DMAX = QXTILE / 16 / QNT;  // loads per thread for X
+    constexpr int DMAW = QWTILE / 16 / QNT;  // loads per thread for W
     static_assert(DMAX * 16 * QNT == QXTILE && DMAW * 16 * QNT == QWTILE, "tiles split over lanes");
     int64_t xoff[DMAX], woff[DMAW];
 #pragma unroll
@@ -157,8 +174,8 @@ __global__ __launch_bounds__(QNT, 2) void qkv_proj_kernel(QkvParams p) {
     // wm*QWM + o - QWN. They are double-buffered in registers: while the
     // products of K-step s run, the operands of K-step s+1 are read, one
     // after each product.
-    constexpr int NO = QWN + QWM;  // 5 operands
-    constexpr int NP = QWN * QWM;  // 6 products
+    constexpr int NO = QWN + QWM;  // operands per K-step
+    constexpr int NP = QWN * QWM;  // products per K-step
     static_assert(NO < NP, "each operand read follows a product");
     auto read_op = [&](const unsigned char* st, int s, int o) __attribute__((always_inline)) -> u32x4 {
         return o < QWN ? operand(st + QXTILE, wn * QWN + o, s) : operand(st, wm * QWM + (o - QWN), s);
@@ -211,10 +228,10 @@ __global__ __launch_bounds__(QNT, 2) void qkv_proj_kernel(QkvParams p) {
     // acc[a][b2] register r of lane (n32, hh): column n = (wn*QWN+a)*32 +
     // blk_row(r, hh) of the tile, row m = (wm*QWM+b2)*32 + n32.
     // An 8-byte write pass covers 16 lanes (16 consecutive rows) on 32
-    // banks; rows QOROW elements (100 words) apart meet in pairs, rows r and
-    // r + 8. Rows with bit 3 set swap the two 8-byte halves of each 16-byte
-    // chunk, which moves them onto the free banks (measured on gfx950: bank
-    // conflict cycles down by two thirds); the store loop swaps them back.
+    // banks; rows QOROW elements apart meet in pairs, rows r and r + 8. Rows
+    // with bit 3 set swap the two 8-byte halves of each 16-byte chunk, which
+    // moves them onto the free banks (measured on gfx950: bank conflict
+    // cycles down by two thirds); the store loop swaps them back.
     T* Ys = reinterpret_cast<T*>(smem);
 #pragma unroll
     for (int a = 0; a < QWN; ++a)
@@ -240,15 +257,43 @@ __global__ __launch_bounds__(QNT, 2) void qkv_proj_kernel(QkvParams p) {
         const int h = j / p.d, c = j - h * p.d;
         const int b = m / p.S, s = m - b * p.S;
         const int64_t dst = p.so.head(b, h) + (int64_t)s * p.so.s + c;
-        // streaming stores: the outputs of all workgroups leave at the end
-        // of the launch at once, which non-temporal stores drain faster
         u32x4 val = *reinterpret_cast<const u32x4*>(Ys + row * QOROW + cc * 8);
         if ((row >> 3) & 1) val = u32x4{val[2], val[3], val[0], val[1]};
+        // streaming stores: the outputs of all workgroups leave at the end
+        // of the launch at once, which non-temporal stores drain faster
         __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(static_cast<T*>(p.out[t]) + dst));
     }
 }
 
+template <typename C>
+int64_t qkv_tiles(int M, int N) {
+    return (int64_t)((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+}
+
+template <typename C>
+hipError_t launch_qkv(const QkvArgs& a, QkvParams p, hipStream_t stream) {
+    p.n_ntiles = (p.N + C::BN - 1) / C::BN;
+    const int64_t grid = qkv_tiles<C>(p.M, p.N);
+    if (grid > 0x7fffffff || grid == 0) return grid == 0 ? hipSuccess : hipErrorInvalidValue;
+    p.remap = (grid % 8 == 0) ? 1 : 0;
+    if (a.dtype == 2)
+        hipLaunchKernelGGL((qkv_proj_kernel<BF16, C>), dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
+    else
+        hipLaunchKernelGGL((qkv_proj_kernel<F16, C>), dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+int qkv_proj_tiling(int M, int N, int n_cu) {
+    // Rounds of workgroups over the CUs for each tiling; tiling 1 costs about
+    // 1.1 rounds of tiling 0 per round (measured on gfx950: 375 against 457 us
+    // for M 16384, N 6144, D 2048, where it needs 6 rounds against 8).
+    const int64_t cu = n_cu > 0 ? n_cu : 256;
+    const int64_t r0 = (qkv_tiles<QTiling0>(M, N) + QTiling0::WPC * cu - 1) / (QTiling0::WPC * cu);
+    const int64_t r1 = (qkv_tiles<QTiling1>(M, N) + QTiling1::WPC * cu - 1) / (QTiling1::WPC * cu);
+    return 11 * r1 < 10 * r0 ? 1 : 0;
+}
 
 hipError_t run_qkv_proj(const QkvArgs& a, hipStream_t stream) {
     QkvParams p;
@@ -264,15 +309,12 @@ hipError_t run_qkv_proj(const QkvArgs& a, hipStream_t stream) {
     p.H = a.H;
     p.d = a.d;
     p.so = make_strides(a.layout, a.H, a.S, a.d);
-    p.n_ntiles = (p.N + QBN - 1) / QBN;
-    const int64_t grid = (int64_t)((p.M + QBM - 1) / QBM) * p.n_ntiles;
-    if (grid > 0x7fffffff || grid == 0) return grid == 0 ? hipSuccess : hipErrorInvalidValue;
-    p.remap = (grid % 8 == 0) ? 1 : 0;
-    if (a.dtype == 2)
-        hipLaunchKernelGGL(qkv_proj_kernel<BF16>, dim3((unsigned)grid), dim3(QNT), 0, stream, p);
-    else
-        hipLaunchKernelGGL(qkv_proj_kernel<F16>, dim3((unsigned)grid), dim3(QNT), 0, stream, p);
-    return hipGetLastError();
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        n_cu = 0;
+    return qkv_proj_tiling(p.M, p.N, n_cu) == 1 ? launch_qkv<QTiling1>(a, p, stream)
+                                               : launch_qkv<QTiling0>(a, p, stream);
 }
 
 }  // namespace attn

@@ -283,6 +283,27 @@ def test_tile_choice_covers_every_shape(lib):
     assert lib.attn_fwd_tile_choice(0, 1, 1, 1, 64, BF16, 0, ctypes.byref(t)) == E_SHAPE
 
 
+def test_qkv_proj_tiling_choice(lib):
+    """The projection's tiling from the round counts on 256 CUs: 128 x 192
+    tiles (two per CU) unless 256 x 256 tiles need clearly fewer rounds."""
+    t = ctypes.c_int(-5)
+    cases = [  # (B, S, H, d, tiling): medium and BERT tokens stay on the first
+        (1, 4096, 16, 64, 0),    # 512 tiles, one round either way
+        (32, 512, 12, 64, 0),    # 1536 tiles: three rounds either way
+        (1, 16384, 32, 64, 1),   # 4096 tiles: eight rounds against six
+        (1, 4096, 20, 64, 1),    # 640 tiles: two rounds against one
+        (1, 1, 1, 8, 0),
+    ]
+    for B, S, H, d, want in cases:
+        assert lib.attn_qkv_proj_tiling(B, S, H, d, 256, ctypes.byref(t)) == OK
+        assert t.value == want, (B, S, H, d, t.value)
+    # with fewer CUs the large-product tiling comes sooner, never for one round
+    assert lib.attn_qkv_proj_tiling(1, 4096, 16, 64, 64, ctypes.byref(t)) == OK and t.value in (0, 1)
+    assert lib.attn_qkv_proj_tiling(1, 4096, 16, 64, 256, None) == E_NULLPTR
+    for bad in ((0, 1, 1, 8, 256), (1, 0, 1, 8, 256), (1, 1, 0, 8, 256), (1, 1, 1, 0, 256), (1, 1, 1, 8, 0)):
+        assert lib.attn_qkv_proj_tiling(*bad, ctypes.byref(t)) == E_SHAPE, bad
+
+
 def test_tile_table_entries():
     """Every entry of the committed table names an existing variant."""
     path = os.path.join(ROOT, "scaled_dot_product_flashattention_amd", "csrc", "tile_table.inc")

@@ -39,6 +39,10 @@ SHAPES = [  # (B, S, D, H, d): column tails, row tails, one and several K steps
     (2, 77, 192, 2, 128),
     (3, 50, 64, 5, 8),
     (1, 512, 1024, 16, 64),
+    # enough 128 x 192 tiles for two rounds over 256 CUs but one of 256 x 256:
+    # the second tiling (exact fit, then row and column tails)
+    (1, 4096, 64, 20, 64),
+    (1, 4000, 128, 21, 64),
 ]
 
 
@@ -56,6 +60,14 @@ def test_qkv_proj_matches_oracle(shape, dtype, layout):
     torch.cuda.synchronize()
     for name, g, wnt in zip("qkv", got, want):
         check(g, wnt, dtype, f"{name}")
+
+
+def test_qkv_proj_shapes_cover_both_tilings():
+    """The shapes above run both tilings of the projection on this GPU."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    used = {sdpa.attn_qkv_proj_tiling(B, S, H, d, n_cu) for B, S, D, H, d in SHAPES}
+    say(f"tilings used on {n_cu} CUs: {sorted(used)}")
+    assert used == {0, 1}
 
 
 @pytest.mark.parametrize("layout", ["bhsd", "bshd"])
