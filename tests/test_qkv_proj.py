@@ -43,6 +43,7 @@ SHAPES = [  # (B, S, D, H, d): column tails, row tails, one and several K steps
     # the second tiling (exact fit, then row and column tails)
     (1, 4096, 64, 20, 64),
     (1, 4000, 128, 21, 64),
+    (2, 2000, 64, 21, 64),  # a 256-row tile spans the two batches
 ]
 
 
