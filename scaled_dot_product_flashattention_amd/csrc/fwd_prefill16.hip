@@ -571,8 +571,9 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     // the next iteration.
     // At t = 0 the output product multiplies zero probabilities; at the last
     // tile the score product reads a stale stage and its result is unused.
-    auto iteration = [&](auto par, int t) __attribute__((always_inline)) {
+    auto iteration = [&](auto par, int t, auto stg) __attribute__((always_inline)) {
         constexpr int B = decltype(par)::value;
+        constexpr int SG = decltype(stg)::value;  // stage of tile t when a constant (-1: from t)
         SAcc& s_cur = s_buf[B];
         SAcc& s_nxt = s_buf[B ^ 1];
         PAcc& p_cur = pq[B];
@@ -592,8 +593,9 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
             barrier_nofence();
             if (t + P < ntiles) issue_tile(t + P);
         }
-        const unsigned char* kt = stage(t + 1);
-        const unsigned char* vt = stage(t > 0 ? t - 1 : 0);
+        const unsigned char* kt = SG >= 0 ? smem + ((SG + 1) % NST) * STAGE_B : stage(t + 1);
+        const unsigned char* vt = SG >= 0 ? (t > 0 ? smem + ((SG + NST - 1) % NST) * STAGE_B : smem)
+                                          : stage(t > 0 ? t - 1 : 0);
         if (wkey0(t) + KBW * 32 > wave_lim_min) mask_scores(s_cur, t);
 #pragma unroll
         for (int gq = 0; gq < NQ; ++gq) l_old[gq] = l_run[gq];
@@ -664,7 +666,13 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
 #pragma unroll
         for (int gq = 0; gq < NQ; ++gq) l_run[gq] = lacc[gq][0];
         fix_range(s_cur, p_cur);
-        read_v_carry(t);
+        if constexpr (SG >= 0) {
+#pragma unroll
+            for (int f = 0; f < LA && f < NPV; ++f)
+                if (f % NQ == 0) read_vop(f / NQ, smem + SG * STAGE_B);
+        } else {
+            read_v_carry(t);
+        }
     };
 
     // The Q operands and tile 0 load together (one wait covers both); the
@@ -708,11 +716,24 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     }
     // register set 0 serves the even tiles (the BAR2 barrier relies on it)
     int t = 0;
-    for (; t + 1 < ntiles; t += 2) {
-        iteration(int_c<0>{}, t);
-        iteration(int_c<1>{}, t + 1);
+    // A 4-stage ring within the 64 KiB reach of the ds_read immediate offset
+    // runs four tiles per trip with each stage index a constant: every
+    // operand address is then a per-lane base plus an immediate, and the
+    // loop issues no address additions (measured on gfx950: 4 % faster on
+    // those variants; the three-per-SIMD variant spills in that form).
+    if constexpr (NST == 4 && NST * STAGE_B <= 65536 && OCC == 2) {
+        for (; t + 4 <= ntiles; t += 4) {
+            iteration(int_c<0>{}, t, int_c<0>{});
+            iteration(int_c<1>{}, t + 1, int_c<1>{});
+            iteration(int_c<0>{}, t + 2, int_c<2>{});
+            iteration(int_c<1>{}, t + 3, int_c<3>{});
+        }
     }
-    if (t < ntiles) iteration(int_c<0>{}, t);
+    for (; t + 1 < ntiles; t += 2) {
+        iteration(int_c<0>{}, t, int_c<-1>{});
+        iteration(int_c<1>{}, t + 1, int_c<-1>{});
+    }
+    if (t < ntiles) iteration(int_c<0>{}, t, int_c<-1>{});
     if (ntiles > 0) {
         // products of the last tile (its first V operands came with the carry)
 #pragma unroll
