@@ -317,11 +317,13 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     // rows, and the offsets of pass 0 are computed once.
     constexpr int RPP = NIT / CPR;
     static_assert(RPP % 16 == 0, "swizzle period must divide the rows per pass");
-    // At head size 128 the loads of a whole tile take a wave-uniform base in
-    // SGPRs and per-pass 32-bit byte offsets (rows below DMA1 * RPP), so no
-    // vector instruction computes an address (measured on gfx950: 2-3 %
-    // faster there; at head size 64, where four waves issue twice the loads,
+    // When every wave issues loads, those of a whole tile take a
+    // wave-uniform base in SGPRs and per-pass 32-bit byte offsets (rows below
+    // DMA1 * RPP), so no vector instruction computes an address (measured on
+    // gfx950: 2-3 % faster at head size 128, 1 % on the four-wave variants at
+    // head size 64; where the four waves of key half 0 issue twice the loads,
     // 64-bit per-lane addresses measured 1 % faster).
+    constexpr bool DMA_SGPR = NIW == 4 * KSPLIT;
     int64_t koff, voff;
     uint32_t kofb[DMA1], vofb[DMA1];
     {
@@ -345,7 +347,7 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
             const T* vt = vp + key0 * p.sk.s;
 #pragma unroll
             for (int i = 0; i < DMA1; ++i) {
-                if constexpr (D == 128) {
+                if constexpr (DMA_SGPR) {
                     dma16_sb(kt, kofb[i], st + i * NIT * 16);
                     dma16_sb(vt, vofb[i], st + i * NIT * 16 + TILE_B);
                 } else {
