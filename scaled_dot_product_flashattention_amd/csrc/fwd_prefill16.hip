@@ -43,7 +43,10 @@
 //     halves, the waves of half 0, which run ahead of their SIMD partners).
 //     Both sit in LDS row-major with their 16-byte chunks XOR-swizzled per
 //     row so that the K operand reads (ds_read_b128) and the transposing V
-//     operand reads (ds_read_b64_tr_b16) are free of bank conflicts.
+//     operand reads (ds_read_b64_tr_b16) are free of bank conflicts; the K
+//     tiles of every stage come first, then the V tiles, so that when each
+//     tensor's ring fits 64 KiB every operand address is a per-lane base plus
+//     an immediate offset (with the key loop unrolled over the stages).
 //   * KSPLIT = 2: two groups of 4 waves take the two key halves of every
 //     tile for the same queries (each key operand then feeds two query
 //     blocks), and merge their (m, l, O) through LDS at the end. Their Q
@@ -59,6 +62,8 @@
 //   * Workgroups of one head stay on one XCD (its L2 then serves every re-read
 //     of that head's K/V); causal tiles start longest-first, across all the
 //     heads of an XCD when their K/V are small enough to share its L2.
+#include <utility>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -78,6 +83,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 template <int V> using int_c = std::integral_constant<int, V>;
+
+// f(int_c<K>) for K = 0, 1, ... in order.
+template <typename F, int... K>
+__device__ __forceinline__ void for_each_stage(F&& f, std::integer_sequence<int, K...>) {
+    (f(int_c<K>{}), ...);
+}
 
 struct Prefill16Params {
     const void* q;
@@ -104,11 +115,14 @@ struct Prefill16Params {
     int chunk;
 };
 
-// LDS of one workgroup: the K/V ring, reused for the output staging rows
-// (D + 8 elements per query) and, with two key halves, for the merge of the
-// halves' (O, m, l) in fp32.
+// LDS of one workgroup: the K/V ring (then, with two key halves, the staged
+// Q rows when they fit beside it in 160 KiB), reused for the output staging
+// rows (D + 8 elements per query) and, with two key halves, for the merge of
+// the halves' (O, m, l) in fp32.
 constexpr int lds_bytes16(int D, int NQ, int BN, int NST, int KSPLIT) {
-    const int ring = NST * 2 * BN * D * 2;
+    const int ring0 = NST * 2 * BN * D * 2;
+    const int qb = 4 * 32 * NQ * D * 2;  // staged Q rows (two key halves)
+    const int ring = ring0 + ((KSPLIT == 2 && ring0 + qb <= 160 * 1024) ? qb : 0);
     const int out = 4 * 32 * NQ * (D + 8) * 2;
     const int mrg = KSPLIT == 2 ? 8 * (NQ * (D / 64) * 16 + 2 * NQ) * 64 * 4 : 0;
     const int a = ring > out ? ring : out;
@@ -179,7 +193,8 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     constexpr int RB = D * 2;                      // bytes per K/V row
     constexpr int CPR = RB / 16;                   // 16-byte chunks per row
     constexpr int TILE_B = BN * RB;
-    constexpr int STAGE_B = 2 * TILE_B;            // K tile, then V tile
+    constexpr int STAGE_B = TILE_B;                // stage stride: K tiles of every stage, then V tiles
+    constexpr int VOFF = NST * TILE_B;             // V tile of stage g at VOFF + g * TILE_B
     // At head size 64 with two key halves only the four waves of half 0
     // issue the DMA loads: they win issue arbitration against their SIMD
     // partners of half 1 and reach each barrier first, so the stall of
@@ -259,11 +274,10 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     u32x4 qop[NQ][D / 16];
     // With two key halves both waves of a query group need the same Q: the
     // first four waves load the workgroup's BM rows once, by DMA, into LDS
-    // stages P.. (untouched until the first iteration's barrier), and every
-    // wave reads its operands from there after the prologue's barrier.
-    constexpr bool QLDS = KSPLIT == 2;
-    constexpr int QOFF = P * STAGE_B;  // LDS byte offset of the staged Q rows
-    static_assert(!QLDS || QOFF + BM * RB <= NST * STAGE_B, "staged Q must fit the free stages");
+    // after the K/V ring (where they fit; else each wave loads its own), and
+    // every wave reads its operands from there after the prologue's barrier.
+    constexpr bool QLDS = KSPLIT == 2 && 2 * NST * TILE_B + BM * RB <= 160 * 1024;
+    constexpr int QOFF = 2 * NST * TILE_B;  // LDS byte offset of the staged Q rows
     if constexpr (QLDS) {
         if (wave < 4) {
             const uint32_t st = __builtin_amdgcn_readfirstlane(
@@ -349,10 +363,10 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
             for (int i = 0; i < DMA1; ++i) {
                 if constexpr (DMA_SGPR) {
                     dma16_sb(kt, kofb[i], st + i * NIT * 16);
-                    dma16_sb(vt, vofb[i], st + i * NIT * 16 + TILE_B);
+                    dma16_sb(vt, vofb[i], st + i * NIT * 16 + VOFF);
                 } else {
                     dma16(kt + koff + (int64_t)i * RPP * p.sk.s, st + i * NIT * 16);
-                    dma16(vt + voff + (int64_t)i * RPP * p.sk.s, st + i * NIT * 16 + TILE_B);
+                    dma16(vt + voff + (int64_t)i * RPP * p.sk.s, st + i * NIT * 16 + VOFF);
                 }
             }
         } else {
@@ -362,7 +376,7 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
                 const int row = slot / CPR, pc = slot - row * CPR;
                 const int64_t key = min(key0 + row, nb - 1);
                 dma16(kp + key * p.sk.s + (pc ^ swz_k<D>(row)) * 8, st + i * NIT * 16);
-                dma16(vp + key * p.sk.s + (pc ^ swz_v<D>(row)) * 8, st + i * NIT * 16 + TILE_B);
+                dma16(vp + key * p.sk.s + (pc ^ swz_v<D>(row)) * 8, st + i * NIT * 16 + VOFF);
             }
         }
     };
@@ -418,7 +432,46 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
         kop[o] = k_operand(kt, kb0 + o % KBW, o / KBW);
     };
     auto read_vop = [&](int o, const unsigned char* vt) __attribute__((always_inline)) {
-        vop[o] = v_operand(vt + TILE_B, kb0 + o / (2 * (D / 32)), (o / (D / 32)) % 2, o % (D / 32));
+        vop[o] = v_operand(vt + VOFF, kb0 + o / (2 * (D / 32)), (o / (D / 32)) % 2, o % (D / 32));
+    };
+    // Per-lane LDS addresses of the operand reads for loops with constant
+    // stage indices: K operand of K-step s at klb[s] + stage * TILE_B + (key
+    // block) * 32 * RB; V operand of head-dimension block db at vlb[db] +
+    // VOFF + stage * TILE_B + (key block * 32 + 16 u + 8 hf) * RB. The key
+    // block and u, hf offsets keep the swizzles (they move whole rows within
+    // a swizzle period).
+    constexpr int NKL = D / 16, NVL = D / 32;
+    constexpr int KOFF_MAX = (NST - 1) * TILE_B + (KBW - 1) * 32 * RB;
+    constexpr int VOFF_MAX = (NST - 1) * TILE_B + ((KBW - 1) * 32 + 24) * RB;
+    constexpr bool UNROLL = NST % 2 == 0 && KOFF_MAX < 65536 && VOFF_MAX < 65536 && OCC == 2;
+    uint32_t klb[NKL], vlb[NVL];
+    {
+        const uint32_t base = (uint32_t)(uintptr_t)(lds_void*)smem;
+        const int krow = kb0 * 32 + n32;
+#pragma unroll
+        for (int s2 = 0; s2 < NKL; ++s2) klb[s2] = base + krow * RB + (((2 * s2 + hh) ^ swz_k<D>(krow)) << 4);
+        const int vrow = kb0 * 32 + 4 * hh + e_tr;
+#pragma unroll
+        for (int db = 0; db < NVL; ++db) {
+            const int lc = db * 4 + 2 * (grp & 1) + (q_tr >> 1);
+            vlb[db] = base + VOFF + vrow * RB + ((lc ^ swz_v<D>(vrow)) << 4) + 8 * (q_tr & 1);
+        }
+    }
+    typedef __attribute__((address_space(3))) const u32x4 lds_cu32x4;
+    auto read_kop_c = [&](int o, int stg) __attribute__((always_inline)) {
+        const int kb = o % KBW, s2 = o / KBW;
+        kop[o] = *(lds_cu32x4*)(uintptr_t)(klb[s2] + stg * TILE_B + kb * 32 * RB);
+    };
+    auto read_vop_c = [&](int o, int stg) __attribute__((always_inline)) {
+        const int kb = o / (2 * (D / 32)), u = (o / (D / 32)) % 2, db = o % (D / 32);
+        u32x2 part[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const uint32_t a = vlb[db] + stg * TILE_B + (kb * 32 + 16 * u + 8 * hf) * RB;
+            const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)a);
+            part[hf] = __builtin_bit_cast(u32x2, r);
+        }
+        vop[o] = u32x4{part[0][0], part[0][1], part[1][0], part[1][1]};
     };
     // the V operands due in the first LA slots of the next iteration
     auto read_v_carry = [&](int tile) __attribute__((always_inline)) {
@@ -595,9 +648,18 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
             barrier_nofence();
             if (t + P < ntiles) issue_tile(t + P);
         }
-        const unsigned char* kt = SG >= 0 ? smem + ((SG + 1) % NST) * STAGE_B : stage(t + 1);
-        const unsigned char* vt = SG >= 0 ? (t > 0 ? smem + ((SG + NST - 1) % NST) * STAGE_B : smem)
-                                          : stage(t > 0 ? t - 1 : 0);
+        const unsigned char* kt = stage(t + 1);
+        const unsigned char* vt = stage(t > 0 ? t - 1 : 0);
+        constexpr int KSG = SG >= 0 ? (SG + 1) % NST : 0;        // stage of tile t+1
+        constexpr int VSG = SG >= 0 ? (SG + NST - 1) % NST : 0;  // stage of tile t-1
+        if constexpr (SG >= 0) {
+            // fresh names for the lane addresses each iteration, so that no
+            // stage's sums of them are kept in registers across the loop
+#pragma unroll
+            for (int j = 0; j < NKL; ++j) asm volatile("" : "+v"(klb[j]));
+#pragma unroll
+            for (int j = 0; j < NVL; ++j) asm volatile("" : "+v"(vlb[j]));
+        }
         if (wkey0(t) + KBW * 32 > wave_lim_min) mask_scores(s_cur, t);
 #pragma unroll
         for (int gq = 0; gq < NQ; ++gq) l_old[gq] = l_run[gq];
@@ -651,9 +713,17 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
         for (int i = 0; i < NM; ++i) {
             // operand reads for slot i + LA
             const int f = i + LA;
-            if (f < NPV && f % NQ == 0) read_vop(f / NQ, vt);
-            if (f >= NPV && f < NM && (f - NPV) % NQ == 0) read_kop((f - NPV) / NQ, kt);
-            if (i < LA && i >= NPV && (i - NPV) % NQ == 0) read_kop((i - NPV) / NQ, kt);
+            if constexpr (SG >= 0) {
+                // at t = 0 the output product multiplies zero probabilities:
+                // any stage will do (stage 0 holds tile 0)
+                if (f < NPV && f % NQ == 0) read_vop_c(f / NQ, VSG);
+                if (f >= NPV && f < NM && (f - NPV) % NQ == 0) read_kop_c((f - NPV) / NQ, KSG);
+                if (i < LA && i >= NPV && (i - NPV) % NQ == 0) read_kop_c((i - NPV) / NQ, KSG);
+            } else {
+                if (f < NPV && f % NQ == 0) read_vop(f / NQ, vt);
+                if (f >= NPV && f < NM && (f - NPV) % NQ == 0) read_kop((f - NPV) / NQ, kt);
+                if (i < LA && i >= NPV && (i - NPV) % NQ == 0) read_kop((i - NPV) / NQ, kt);
+            }
             if (i < NPV) pv_mfma(i, p_prv); else qk_mfma(i - NPV, s_nxt);
             stage_exp(i);
             stage_shift(i + 1);
@@ -671,7 +741,7 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
         if constexpr (SG >= 0) {
 #pragma unroll
             for (int f = 0; f < LA && f < NPV; ++f)
-                if (f % NQ == 0) read_vop(f / NQ, smem + SG * STAGE_B);
+                if (f % NQ == 0) read_vop_c(f / NQ, SG);
         } else {
             read_v_carry(t);
         }
@@ -680,6 +750,14 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     // The Q operands and tile 0 load together (one wait covers both); the
     // Q loads go first, as they do not wait for the key length. The rest of
     // the ring goes out after the wait.
+    if constexpr (UNROLL) {
+        // the unrolled loop's first output product reads the V stage of
+        // "tile -1" (stage NST - 1) against zero probabilities: clear it so
+        // that no stale bits meet the zeros (the barrier before the first
+        // iteration orders these writes)
+        u32x4* vz = reinterpret_cast<u32x4*>(smem + VOFF + (NST - 1) * TILE_B);
+        for (int i = tid; i < TILE_B / 16; i += 256 * KSPLIT) vz[i] = u32x4{0u, 0u, 0u, 0u};
+    }
     if (ntiles > 0) issue_tile(0);
     wait_vmcnt<0>();
     for (int t = 1; t < min(P, ntiles); ++t) issue_tile(t);
@@ -718,17 +796,20 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     }
     // register set 0 serves the even tiles (the BAR2 barrier relies on it)
     int t = 0;
-    // A 4-stage ring within the 64 KiB reach of the ds_read immediate offset
-    // runs four tiles per trip with each stage index a constant: every
-    // operand address is then a per-lane base plus an immediate, and the
-    // loop issues no address additions (measured on gfx950: 4 % faster on
-    // those variants; the three-per-SIMD variant spills in that form).
-    if constexpr (NST == 4 && NST * STAGE_B <= 65536 && OCC == 2) {
-        for (; t + 4 <= ntiles; t += 4) {
-            iteration(int_c<0>{}, t, int_c<0>{});
-            iteration(int_c<1>{}, t + 1, int_c<1>{});
-            iteration(int_c<0>{}, t + 2, int_c<2>{});
-            iteration(int_c<1>{}, t + 3, int_c<3>{});
+    // Rings whose K (and V) tiles fit the 64 KiB reach of the ds_read
+    // immediate offset run NST tiles per trip with each stage index a
+    // constant: every operand address is then a per-lane base plus an
+    // immediate, and the loop issues no address additions (measured on
+    // gfx950: 1-8 % faster on those variants; the three-per-SIMD variant
+    // spills in that form and keeps the plain loop).
+    if constexpr (UNROLL) {
+        for (; t + NST <= ntiles; t += NST) {
+            for_each_stage(
+                [&](auto kc) __attribute__((always_inline)) {
+                    constexpr int K = decltype(kc)::value;
+                    iteration(int_c<K & 1>{}, t + K, int_c<K>{});
+                },
+                std::make_integer_sequence<int, NST>{});
         }
     }
     for (; t + 1 < ntiles; t += 2) {
