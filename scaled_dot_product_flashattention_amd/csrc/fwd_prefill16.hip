@@ -331,20 +331,20 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     // rows, and the offsets of pass 0 are computed once.
     constexpr int RPP = NIT / CPR;
     static_assert(RPP % 16 == 0, "swizzle period must divide the rows per pass");
-    // When every wave issues loads, those of a whole tile take a
-    // wave-uniform base in SGPRs and per-pass 32-bit byte offsets (rows below
-    // DMA1 * RPP), so no vector instruction computes an address (measured on
-    // gfx950: 2-3 % faster at head size 128, 1 % on the four-wave variants at
-    // head size 64; where the four waves of key half 0 issue twice the loads,
-    // 64-bit per-lane addresses measured 1 % faster).
-    constexpr bool DMA_SGPR = NIW == 4 * KSPLIT;
-    int64_t koff, voff;
+    // The loads of a whole tile take a wave-uniform 64-bit base in SGPRs and
+    // a 32-bit byte offset per lane, so no vector instruction computes an
+    // address. At head size 128 each pass has its own offset register; at
+    // head size 64 one offset serves every pass and the pass's rows go into
+    // the scalar base, which saves the registers whose spills (with a reload
+    // whose wait drained the DMA queue) cost the eight-wave variant 2.5 %
+    // (measured on gfx950; at head size 128 per-pass offsets were 1 % faster).
+    constexpr bool DMA_ONE_OFF = D == 64;
     uint32_t kofb[DMA1], vofb[DMA1];
     {
         const int slot = tid & (NIT - 1);
         const int row = slot / CPR, pc = slot - row * CPR;
-        koff = row * p.sk.s + (pc ^ swz_k<D>(row)) * 8;
-        voff = row * p.sk.s + (pc ^ swz_v<D>(row)) * 8;
+        const int64_t koff = row * p.sk.s + (pc ^ swz_k<D>(row)) * 8;
+        const int64_t voff = row * p.sk.s + (pc ^ swz_v<D>(row)) * 8;
 #pragma unroll
         for (int i = 0; i < DMA1; ++i) {
             kofb[i] = (uint32_t)((koff + (int64_t)i * RPP * p.sk.s) * 2);
@@ -361,18 +361,23 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
             const T* vt = vp + key0 * p.sk.s;
 #pragma unroll
             for (int i = 0; i < DMA1; ++i) {
-                if constexpr (DMA_SGPR) {
+                if constexpr (DMA_ONE_OFF) {
+                    dma16_sb(kt + (int64_t)i * RPP * p.sk.s, kofb[0], st + i * NIT * 16);
+                    dma16_sb(vt + (int64_t)i * RPP * p.sk.s, vofb[0], st + i * NIT * 16 + VOFF);
+                } else {
                     dma16_sb(kt, kofb[i], st + i * NIT * 16);
                     dma16_sb(vt, vofb[i], st + i * NIT * 16 + VOFF);
-                } else {
-                    dma16(kt + koff + (int64_t)i * RPP * p.sk.s, st + i * NIT * 16);
-                    dma16(vt + voff + (int64_t)i * RPP * p.sk.s, st + i * NIT * 16 + VOFF);
                 }
             }
         } else {
+            // A partial last tile recomputes its addresses from the thread
+            // index: the opaque copy keeps the compiler from hoisting them
+            // out of the key loop into registers held for the whole loop.
+            int tid_r = tid;
+            asm volatile("" : "+v"(tid_r));
 #pragma unroll
             for (int i = 0; i < DMA1; ++i) {
-                const int slot = i * NIT + tid;
+                const int slot = i * NIT + tid_r;
                 const int row = slot / CPR, pc = slot - row * CPR;
                 const int64_t key = min(key0 + row, nb - 1);
                 dma16(kp + key * p.sk.s + (pc ^ swz_k<D>(row)) * 8, st + i * NIT * 16);
@@ -640,8 +645,13 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
             if constexpr (B == 0) {
                 if (t + 1 < ntiles) wait_tile(min(t + 2, ntiles - 1), min(t + P - 1, ntiles - 1));
                 barrier_nofence();
-                if (t + P < ntiles) issue_tile(t + P);
-                if (t + P + 1 < ntiles) issue_tile(t + P + 1);
+                // one wave-uniform guard for both loads (per call, the
+                // compiler kept a copy of it in a VGPR, spilled, and reloaded
+                // it after the barrier, a reload whose wait drained the DMA)
+                if (wave < NIW) {
+                    if (t + P < ntiles) issue_tile(t + P);
+                    if (t + P + 1 < ntiles) issue_tile(t + P + 1);
+                }
             }
         } else {
             if (t + 1 < ntiles) wait_tile(t + 1, min(t + P - 1, ntiles - 1));
@@ -652,6 +662,7 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
         const unsigned char* vt = stage(t > 0 ? t - 1 : 0);
         constexpr int KSG = SG >= 0 ? (SG + 1) % NST : 0;        // stage of tile t+1
         constexpr int VSG = SG >= 0 ? (SG + NST - 1) % NST : 0;  // stage of tile t-1
+        const int ksr = (t + 1) % NST, vsr = (t > 0 ? t - 1 : 0) % NST;
         if constexpr (SG >= 0) {
             // fresh names for the lane addresses each iteration, so that no
             // stage's sums of them are kept in registers across the loop
@@ -719,6 +730,14 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
                 if (f < NPV && f % NQ == 0) read_vop_c(f / NQ, VSG);
                 if (f >= NPV && f < NM && (f - NPV) % NQ == 0) read_kop_c((f - NPV) / NQ, KSG);
                 if (i < LA && i >= NPV && (i - NPV) % NQ == 0) read_kop_c((i - NPV) / NQ, KSG);
+            } else if constexpr (UNROLL) {
+                // the leftover tiles after the unrolled trips read through
+                // the same lane bases with a run-time stage offset: no lane
+                // index then stays live across the unrolled loop (it was
+                // spilled there, and the spills cost HBM traffic)
+                if (f < NPV && f % NQ == 0) read_vop_c(f / NQ, vsr);
+                if (f >= NPV && f < NM && (f - NPV) % NQ == 0) read_kop_c((f - NPV) / NQ, ksr);
+                if (i < LA && i >= NPV && (i - NPV) % NQ == 0) read_kop_c((i - NPV) / NQ, ksr);
             } else {
                 if (f < NPV && f % NQ == 0) read_vop(f / NQ, vt);
                 if (f >= NPV && f < NM && (f - NPV) % NQ == 0) read_kop((f - NPV) / NQ, kt);
@@ -738,10 +757,10 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
 #pragma unroll
         for (int gq = 0; gq < NQ; ++gq) l_run[gq] = lacc[gq][0];
         fix_range(s_cur, p_cur);
-        if constexpr (SG >= 0) {
+        if constexpr (SG >= 0 || UNROLL) {
 #pragma unroll
             for (int f = 0; f < LA && f < NPV; ++f)
-                if (f % NQ == 0) read_vop_c(f / NQ, SG);
+                if (f % NQ == 0) read_vop_c(f / NQ, SG >= 0 ? SG : t % NST);
         } else {
             read_v_carry(t);
         }
@@ -820,8 +839,11 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     if (ntiles > 0) {
         // products of the last tile (its first V operands came with the carry)
 #pragma unroll
-        for (int o = 0; o < NV; ++o)
-            if (o * NQ >= LA) read_vop(o, stage(ntiles - 1));
+        for (int o = 0; o < NV; ++o) {
+            if (o * NQ < LA) continue;
+            if constexpr (UNROLL) read_vop_c(o, (ntiles - 1) % NST);
+            else read_vop(o, stage(ntiles - 1));
+        }
         if ((ntiles - 1) & 1) {
 #pragma unroll
             for (int i = 0; i < NPV; ++i) pv_mfma(i, pq[1]);
