@@ -21,7 +21,7 @@ BHSD, BSHD = 0, 1
 F32, F16, BF16 = 0, 1, 2
 
 
-N_TILES = {64: 5, 128: 4}  # tile variants of the 16-bit fused kernel per head size
+N_TILES = {64: 6, 128: 4}  # tile variants of the 16-bit fused kernel per head size
 
 
 def SPLIT(g):  # heads in groups of g

@@ -21,7 +21,7 @@ from scaled_dot_product_flashattention_amd.inputs import WORKLOADS, generate
 pytestmark = pytest.mark.gpu
 
 W = WORKLOADS
-N_TILES = {64: 5, 128: 4}
+N_TILES = {64: 6, 128: 4}
 CASES = [(dt, d, t) for dt, d in (("bf16", 64), ("f16", 64), ("bf16", 128), ("f16", 128))
          for t in range(N_TILES[d])]
 # name: (B, H, Sq, Sk, causal, kv_len range, layout, n_split, extra workload fields)

@@ -12,7 +12,7 @@ from scaled_dot_product_flashattention_amd.inputs import WORKLOADS
 
 pytestmark = pytest.mark.gpu
 
-N_TILES = {64: 5, 128: 4}
+N_TILES = {64: 6, 128: 4}
 
 
 def cases(n=128, seed=20261202):

@@ -17,7 +17,7 @@ from scaled_dot_product_flashattention_amd.inputs import WORKLOADS, generate
 pytestmark = pytest.mark.gpu
 
 W = WORKLOADS
-N_TILES = {64: 5, 128: 4}  # variants per head size (the ABI tests check the library agrees)
+N_TILES = {64: 6, 128: 4}  # variants per head size (the ABI tests check the library agrees)
 CASES = [(dt, d, t) for dt, d in (("bf16", 64), ("f16", 64), ("bf16", 128), ("f16", 128))
          for t in range(N_TILES[d])]
 SHAPES = {  # name: (B, H, Sq, Sk, causal, kv_len range, layout, extra workload fields)
