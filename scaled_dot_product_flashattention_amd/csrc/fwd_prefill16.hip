@@ -1052,8 +1052,8 @@ struct Variant16 {
 const Variant16 kVariants64[] = {
     ATTN_VARIANT16(64, 1, 64, 5, 1, 2),  // 0: 128 queries x 64 keys, 4 waves
     ATTN_VARIANT16(64, 1, 64, 4, 1, 2),  // 1: same, shorter ring
-    ATTN_VARIANT16(64, 2, 64, 8, 2, 2),  // 2: 256 queries, 8 waves in two key halves
-    ATTN_VARIANT16(64, 1, 64, 8, 2, 2),  // 3: 128 queries, 8 waves in two key halves
+    ATTN_VARIANT16(64, 2, 64, 6, 2, 2),  // 2: 256 queries, 8 waves in two key halves
+    ATTN_VARIANT16(64, 1, 64, 6, 2, 2),  // 3: 128 queries, 8 waves in two key halves
     ATTN_VARIANT16(64, 1, 32, 4, 1, 3),  // 4: 128 queries x 32 keys, 4 waves, three per SIMD
     ATTN_VARIANT16(64, 2, 32, 6, 1, 2),  // 5: 256 queries x 32 keys, 4 waves, two per SIMD
 };

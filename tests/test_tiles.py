@@ -93,7 +93,7 @@ def test_table_choice_is_the_default_path():
 
 
 # Key walks of exactly 1 .. 6 tiles (and a ragged last tile): the pipeline's
-# ends, and with rings of 8 stages the barrier taken at even tiles only.
+# ends, and with rings of six stages the barrier taken at even tiles only.
 WALKS = [(d, t, sk) for d in (64, 128) for t in range(N_TILES[d]) for sk in (64, 128, 191, 256, 320, 383)]
 
 
