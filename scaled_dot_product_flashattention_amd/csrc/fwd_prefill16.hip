@@ -448,7 +448,7 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     constexpr int NKL = D / 16, NVL = D / 32;
     constexpr int KOFF_MAX = (NST - 1) * TILE_B + (KBW - 1) * 32 * RB;
     constexpr int VOFF_MAX = (NST - 1) * TILE_B + ((KBW - 1) * 32 + 24) * RB;
-    constexpr bool UNROLL = NST % 2 == 0 && KOFF_MAX < 65536 && VOFF_MAX < 65536 && OCC == 2;
+    constexpr bool UNROLL = NST % 2 == 0 && KOFF_MAX < 65536 && VOFF_MAX < 65536;
     uint32_t klb[NKL], vlb[NVL];
     {
         const uint32_t base = (uint32_t)(uintptr_t)(lds_void*)smem;
@@ -819,8 +819,8 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
     // immediate offset run NST tiles per trip with each stage index a
     // constant: every operand address is then a per-lane base plus an
     // immediate, and the loop issues no address additions (measured on
-    // gfx950: 1-8 % faster on those variants; the three-per-SIMD variant
-    // spills in that form and keeps the plain loop).
+    // gfx950: 1-8 % faster on those variants, 2-4 % on the three-per-SIMD
+    // one once the DMA addressing no longer held per-lane 64-bit pointers).
     if constexpr (UNROLL) {
         for (; t + NST <= ntiles; t += NST) {
             for_each_stage(
