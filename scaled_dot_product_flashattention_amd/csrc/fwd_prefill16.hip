@@ -1035,9 +1035,7 @@ hipError_t launch16(const FwdArgs& a, hipStream_t stream) {
 
 // ---- tile variants and their choice ----------------------------------------
 // Tile sizes are not probed at run time: the candidates below are compiled in
-// (none spills registers in the products of its key loop at its waves per
-// SIMD; the deepest rings keep a few values that live across the loop, or a
-// base address reloaded once per tile, in scratch), and
+// (none uses scratch memory at its waves per SIMD), and
 // a table made offline by timing every candidate over a grid of shapes
 // (tile_table.inc) names the variant per head size, masking, key length and
 // query rows.
