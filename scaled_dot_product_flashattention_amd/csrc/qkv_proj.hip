@@ -248,20 +248,32 @@ __global__ __launch_bounds__(C::NT, C::WPC) void qkv_proj_kernel(QkvParams p) {
             }
         }
     __syncthreads();
+    // Each thread keeps one 16-byte column chunk of the tile and walks rows
+    // RPS apart: the chunk's tensor, head and column are divided out once,
+    // and the (batch, token) of its rows advance by addition.
+    constexpr int CPW = QBN / 8;    // 16-byte chunks per tile row
+    constexpr int RPS = QNT / CPW;  // rows per sweep of the workgroup
     const int HD = p.H * p.d;
-    for (int cidx = tid; cidx < QBM * (QBN / 8); cidx += QNT) {
-        const int row = cidx / (QBN / 8), cc = cidx % (QBN / 8);
-        const int m = m0 + row, n = n0 + cc * 8;
-        if (m >= p.M || n >= p.N) continue;
+    const int cc = tid % CPW, n = n0 + cc * 8;
+    if (tid < RPS * CPW && n < p.N) {
         const int t = n / HD, j = n - t * HD;
         const int h = j / p.d, c = j - h * p.d;
-        const int b = m / p.S, s = m - b * p.S;
-        const int64_t dst = p.so.head(b, h) + (int64_t)s * p.so.s + c;
-        u32x4 val = *reinterpret_cast<const u32x4*>(Ys + row * QOROW + cc * 8);
-        if ((row >> 3) & 1) val = u32x4{val[2], val[3], val[0], val[1]};
-        // streaming stores: the outputs of all workgroups leave at the end
-        // of the launch at once, which non-temporal stores drain faster
-        __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(static_cast<T*>(p.out[t]) + dst));
+        T* const obase = static_cast<T*>(p.out[t]) + p.so.head(0, h) + c;
+        int row = tid / CPW;
+        int m = m0 + row;
+        int b = m / p.S, s = m - b * p.S;
+        for (; row < QBM && m < p.M; row += RPS, m += RPS) {
+            u32x4 val = *reinterpret_cast<const u32x4*>(Ys + row * QOROW + cc * 8);
+            if ((row >> 3) & 1) val = u32x4{val[2], val[3], val[0], val[1]};
+            // streaming stores: the outputs of all workgroups leave at the end
+            // of the launch at once, which non-temporal stores drain faster
+            __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(obase + b * p.so.b + (int64_t)s * p.so.s));
+            s += RPS;
+            while (s >= p.S) {
+                s -= p.S;
+                ++b;
+            }
+        }
     }
 }
 
