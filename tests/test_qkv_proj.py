@@ -38,6 +38,10 @@ SHAPES = [  # (B, S, D, H, d): column tails, row tails, one and several K steps
     (1, 300, 256, 3, 64),
     (2, 77, 192, 2, 128),
     (3, 50, 64, 5, 8),
+    # sequences shorter than the rows between one thread's stores: several
+    # batches per step of the store loop
+    (9, 7, 64, 2, 64),
+    (40, 1, 128, 3, 32),
     (1, 512, 1024, 16, 64),
     # enough 128 x 192 tiles for two rounds over 256 CUs but one of 256 x 256:
     # the second tiling (exact fit, then row and column tails)
