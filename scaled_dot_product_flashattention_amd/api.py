@@ -263,7 +263,8 @@ def attn_fwd(q, k, v, *, scale=None, causal=False, layout="bhsd", kv_len=None, r
     (B, H, Sq, Sk, d), kv_len, scale, o, lse = _prepare(q, k, v, layout, kv_len, scale, lse,
                                                         return_lse, out)
     dt = dtype_code(q.dtype)
-    nbytes = attn_fwd_workspace_size(B, H, Sq, Sk, d, q.dtype, causal)
+    # a caller's workspace is checked against the plan by the library itself
+    nbytes = 0 if workspace is not None else attn_fwd_workspace_size(B, H, Sq, Sk, d, q.dtype, causal)
     ws = _scratch(nbytes, q.device, workspace)
     rc = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Sq, Sk, d,
                                  scale, int(bool(causal)), layout_code(layout), dt, _ptr(kv_len),
