@@ -974,7 +974,9 @@ __global__ __launch_bounds__(256 * KSPLIT, OCC / KSPLIT) void fwd_prefill16_kern
                 if (qi < p.Sq) {
                     u32x4 val = *reinterpret_cast<const u32x4*>(Os + row * OROW + cc * 8);
                     if ((row >> 3) & 1) val = u32x4{val[2], val[3], val[0], val[1]};
-                    *reinterpret_cast<u32x4*>(op + (int64_t)qi * p.sq.s + cc * 8) = val;
+                    // streaming stores: O is written once and not read here
+                    // (measured on gfx950: 1-3.5 % faster, most on short key walks)
+                    __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(op + (int64_t)qi * p.sq.s + cc * 8));
                 }
             }
         }
