@@ -51,7 +51,7 @@ struct SplitCfg {
     static constexpr int LPK = D / EPL;     // lanes per key row
     static constexpr int KPW = 64 / LPK;    // key rows per wave and load
     static constexpr int NW = 4;            // waves per workgroup
-    static constexpr int U = 4;             // loads in flight per lane and tensor
+    static constexpr int U = 8;             // loads in flight per lane and tensor (8 measured 1.4 % faster than 4 and 6 on gfx950)
     static constexpr int KPI = NW * KPW * U;
     static constexpr int GROUPS = NW * KPW; // independent (m, l, o) states per workgroup
 };
